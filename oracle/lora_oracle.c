@@ -1,0 +1,274 @@
+/*
+ * lora_oracle.c -- plain fp64 CPU oracle for the multi-adapter LoRA linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library; it is built by gcc on its own.
+ *
+ * What it computes (each function cites the passage it follows):
+ *
+ *   y[m,n] = sum_k x[m,k] W[n,k]                                   (base)
+ *          + scale[s] * sum_j B_s[n,j] * ( sum_k A_s[j,k] x[m,k] )  (s = id[m] >= 0)
+ *
+ * with A_s of shape r_s x k applied first and B_s of shape d x r_s second,
+ * scale[s] = alpha_s / r_s stored with the adapter, and id[m] = -1 meaning
+ * "no adapter" (that row gets the base projection only).
+ *
+ * Every sum is an fp64 loop in ascending index order with no blocking, no
+ * fusion and no reordering; the file is compiled with -ffp-contract=off so
+ * each product is rounded before it is added.  Inputs arrive already upcast to
+ * fp64 from their stored precision, so input rounding is not oracle error.
+ */
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ORACLE_MUTANT plants one deliberate mistake (1..9) so the test suite can
+ * show that its pins catch it; the normal build leaves it at 0.  Only the
+ * pin tests build mutants, into a temporary directory. */
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+#define ORACLE_ROW_ADAPTED 0
+#define ORACLE_ROW_NONE 1
+#define ORACLE_ROW_BAD_ID 2
+#define ORACLE_ROW_BAD_RANK 3
+#define ORACLE_ROW_BAD_PAGE 4
+
+/* Element counts of one adapter's two matrices: A is r x k, B is d x r.
+ * "Your LoRA Adapters Are Thrashing Your GPUs", section 02 (parameter
+ * calculation) and "Adapter Residency When One Replica Serves Many
+ * Fine-Tunes", opening section: the adapter holds r(d + k) numbers. */
+int64_t oracle_adapter_params(int64_t d, int64_t k, int64_t r) {
+  int64_t n_a = 0, n_b = 0;
+  for (int64_t j = 0; j < r; ++j) n_a += k; /* rows of A, k each */
+  for (int64_t n = 0; n < d; ++n) n_b += r; /* rows of B, r each */
+  return n_a + n_b;
+}
+
+/* Byte offset of one element inside an adapter's logical byte space in the
+ * paged pool.  The layout reading: A (r x k, row-major) starts at byte 0 and
+ * B (d x r, row-major, row stride r) follows it.  "S-LoRA: what the paper
+ * actually says ...", section "Unified paging": an adapter's weights are
+ * stored in fixed-size blocks; the order inside its space is not given there,
+ * so this plain concatenation is the reading taken.
+ * which = 0 for A[row][col], 1 for B[row][col]. */
+int64_t oracle_adapter_offset(int64_t r, int64_t k, int64_t elem_bytes, int32_t which,
+                              int64_t row, int64_t col) {
+  if (which == 0) return (row * k + col) * elem_bytes;
+  return (r * k + row * r + col) * elem_bytes;
+}
+
+/* Physical byte offset, inside the pool, of logical byte `off` of adapter `a`:
+ * the page index is off / page_bytes, the page table maps it to a physical
+ * page, and the in-page offset is kept.  "S-LoRA: ...", section "Unified
+ * paging" (fixed-size blocks, per-adapter block list).
+ * Writes -1 where the logical page is past max_pages or the table entry is
+ * outside [0, n_pages).  Returns the number of such entries. */
+int64_t oracle_translate(const int32_t *page_table, int32_t max_pages, int64_t page_bytes,
+                         int64_t n_pages, const int32_t *adapter, const int64_t *logical_off,
+                         int64_t n, int64_t *phys_off) {
+  int64_t bad = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t a = adapter[i];
+    int64_t off = logical_off[i];
+    int64_t lp = off / page_bytes;
+    int64_t in_page = off % page_bytes;
+    if (a < 0 || off < 0 || lp >= max_pages) {
+      phys_off[i] = -1;
+      ++bad;
+      continue;
+    }
+    int64_t pp = page_table[a * (int64_t)max_pages + lp];
+    if (pp < 0 || pp >= n_pages) {
+      phys_off[i] = -1;
+      ++bad;
+      continue;
+    }
+#if ORACLE_MUTANT == 6 /* planted: in-page offset dropped */
+    in_page = 0;
+#endif
+    phys_off[i] = pp * page_bytes + in_page;
+  }
+  return bad;
+}
+
+/* Classify every row and build the adapter-sorted packing.
+ *
+ * Row classes: an id of -1 selects no adapter ("LoRA Adapters: Many Models in
+ * One", section "Using it": the base model's name selects none; section "The
+ * model runner's part": a per-token slot index, or none).  Ids outside
+ * [-1, S) are errors; so is a rank outside [0, max_rank], and, for a paged
+ * pool, an adapter whose pages do not fit max_pages or whose table entries
+ * leave [0, n_pages).  Error rows are counted and treated as "none".
+ *
+ * The packing sorts the adapted rows by adapter, keeping row order inside an
+ * adapter, so each adapter's rows are contiguous ("Adapter Residency ...",
+ * section "Batch composition under many adapters"; "S-LoRA: ...", section
+ * "Batched LoRA computation": rows sorted by adapter index, then a segmented
+ * computation).  Segments are the maximal runs of one adapter, listed in
+ * ascending adapter order.
+ *
+ * pool_page_table == NULL means stacked slots (no page checks).
+ * counts[0..2] = bad ids, bad ranks, bad pages.  Returns n_adapted. */
+int64_t oracle_plan(int64_t M, const int32_t *ids, int32_t S, const int32_t *ranks,
+                    int32_t max_rank, const int32_t *pool_page_table, int32_t max_pages,
+                    int64_t n_pages, int64_t page_bytes, int64_t k, int64_t d,
+                    int64_t elem_bytes, int32_t *row_class, int32_t *perm,
+                    int32_t *seg_adapter, int32_t *seg_start, int32_t *seg_len,
+                    int64_t *n_seg_out, int64_t *counts) {
+  counts[0] = counts[1] = counts[2] = 0;
+  for (int64_t m = 0; m < M; ++m) {
+    int32_t id = ids[m];
+    if (id == -1) {
+      row_class[m] = ORACLE_ROW_NONE;
+      continue;
+    }
+    if (id < -1 || id >= S) {
+      row_class[m] = ORACLE_ROW_BAD_ID;
+      counts[0] += 1;
+      continue;
+    }
+    int32_t r = ranks[id];
+    if (r < 0 || r > max_rank) {
+      row_class[m] = ORACLE_ROW_BAD_RANK;
+      counts[1] += 1;
+      continue;
+    }
+    if (pool_page_table != NULL) {
+      int64_t bytes = (int64_t)r * (k + d) * elem_bytes;
+      int64_t pages = (bytes + page_bytes - 1) / page_bytes;
+      int ok = pages <= max_pages;
+      for (int64_t j = 0; ok && j < pages; ++j) {
+        int32_t p = pool_page_table[(int64_t)id * max_pages + j];
+        if (p < 0 || p >= n_pages) ok = 0;
+      }
+      if (!ok) {
+        row_class[m] = ORACLE_ROW_BAD_PAGE;
+        counts[2] += 1;
+        continue;
+      }
+    }
+    row_class[m] = ORACLE_ROW_ADAPTED;
+  }
+
+  /* Stable grouping: walk adapters in ascending order, and for each one walk
+   * the rows in ascending order. */
+  int64_t n_adapted = 0, n_seg = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    int64_t start = n_adapted;
+#if ORACLE_MUTANT == 5 /* planted: rows of one adapter in descending order */
+    for (int64_t m = M - 1; m >= 0; --m) {
+#else
+    for (int64_t m = 0; m < M; ++m) {
+#endif
+      if (row_class[m] == ORACLE_ROW_ADAPTED && ids[m] == s) perm[n_adapted++] = (int32_t)m;
+    }
+    if (n_adapted > start) {
+      seg_adapter[n_seg] = s;
+      seg_start[n_seg] = (int32_t)start;
+      seg_len[n_seg] = (int32_t)(n_adapted - start);
+#if ORACLE_MUTANT == 9 /* planted: segment length off by one */
+      seg_len[n_seg] += 1;
+#endif
+      ++n_seg;
+    }
+  }
+  *n_seg_out = n_seg;
+  return n_adapted;
+}
+
+/* The layer itself.
+ *
+ * Formula: "S-LoRA: ...", section "Batched LoRA computation" (per-request
+ * output is the base term plus (alpha/r) B_k A_k x_i for request i's adapter
+ * k); "Adapter Residency ...", section "What the forward pass has to do
+ * differently" (base over the whole batch, then each adapter's two small
+ * products on its rows only, scaled, and added); "LoRA Adapters: Many Models
+ * in One", section "What an adapter is" (y = W x + (alpha/r) B A x).
+ * The scale is a property of the adapter, one per adapter: "Adapter
+ * Residency ...", same section.
+ *
+ * Layout of the logical adapters: A_s starts at A + a_off[s] and is r_s x k
+ * row-major; B_s starts at B + b_off[s] and is d x r_s row-major.
+ * Rows whose id is -1 or outside [0, S), or whose adapter rank is outside
+ * [0, max_rank], get the base projection only.
+ * x is M x k, W is d x k (out x in), y is M x d, all row-major. */
+void oracle_lora_linear(int64_t M, int64_t k, int64_t d, const double *x, const double *W,
+                        int32_t S, const int32_t *ranks, int32_t max_rank,
+                        const int64_t *a_off, const int64_t *b_off, const double *A,
+                        const double *B, const double *scales, const int32_t *ids,
+                        double *y, int32_t n_threads) {
+  if (n_threads < 1) n_threads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+  for (int64_t m = 0; m < M; ++m) {
+    const double *xm = x + m * k;
+    int32_t s = ids[m];
+#if ORACLE_MUTANT == 7 /* planted: "none" rows take adapter 0 */
+    if (s == -1 && S > 0) s = 0;
+#endif
+    int adapted = (s >= 0 && s < S && ranks[s] >= 0 && ranks[s] <= max_rank);
+    double t[1024];
+    int32_t r = adapted ? ranks[s] : 0;
+    if (r > 1024) adapted = 0; /* never for the shapes used; keeps t in bounds */
+    if (adapted) {
+      const double *As = A + a_off[s];
+      for (int32_t j = 0; j < r; ++j) {
+        double acc = 0.0;
+#if ORACLE_MUTANT == 4 /* planted: A read as k x r (transposed) */
+        for (int64_t kk = 0; kk < k; ++kk) acc += As[kk * r + j] * xm[kk];
+#else
+        for (int64_t kk = 0; kk < k; ++kk) acc += As[(int64_t)j * k + kk] * xm[kk];
+#endif
+        t[j] = acc;
+      }
+#if ORACLE_MUTANT == 8 /* planted: last rank term dropped */
+      if (r > 0) t[r - 1] = 0.0;
+#endif
+    }
+    for (int64_t n = 0; n < d; ++n) {
+      const double *Wn = W + n * k;
+      double base = 0.0;
+      for (int64_t kk = 0; kk < k; ++kk) base += xm[kk] * Wn[kk];
+      if (!adapted) {
+        y[m * d + n] = base;
+        continue;
+      }
+      double delta = 0.0;
+#if ORACLE_MUTANT == 3 /* planted: B read as r x d (transposed) */
+      for (int32_t j = 0; j < r; ++j) delta += B[b_off[s] + (int64_t)j * d + n] * t[j];
+#else
+      const double *Bn = B + b_off[s] + n * (int64_t)r;
+      for (int32_t j = 0; j < r; ++j) delta += Bn[j] * t[j];
+#endif
+#if ORACLE_MUTANT == 1 /* planted: scale dropped */
+      y[m * d + n] = base + delta;
+#elif ORACLE_MUTANT == 2 /* planted: correction subtracted */
+      y[m * d + n] = base - scales[s] * delta;
+#else
+      y[m * d + n] = base + scales[s] * delta;
+#endif
+    }
+  }
+}
+
+/* Threads OpenMP will actually use for n_threads requested. */
+int32_t oracle_threads(int32_t n_threads) {
+#ifdef _OPENMP
+  int32_t used = 1;
+#pragma omp parallel num_threads(n_threads)
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+  }
+  return used;
+#else
+  (void)n_threads;
+  return 1;
+#endif
+}
