@@ -1,0 +1,248 @@
+/*
+ * lora_row.h -- C ABI of liblora_row.so: the multi-adapter LoRA linear layer
+ * on AMD MI355X (gfx950, CDNA4).
+ *
+ * The layer (one shared base weight, a per-row adapter choice):
+ *
+ *   y[m, :] = x[m, :] W^T + scale[s] * (x[m, :] A_s^T) B_s^T     s = adapter_ids[m] >= 0
+ *   y[m, :] = x[m, :] W^T                                         adapter_ids[m] == -1
+ *
+ *   x [M, k], W [d, k] (out x in), A_s [r_s, k], B_s [d, r_s], y [M, d];
+ *   scale[s] = alpha_s / r_s (true rank), stored with the adapter.
+ *
+ * Sources (page title, section):
+ *   - "S-LoRA: what the paper actually says about serving thousands of LoRA
+ *     adapters", "Batched LoRA computation": per-request output is the shared
+ *     base term plus (alpha/r) B_k A_k x_i for that request's adapter k; the
+ *     base is one GEMM over the whole batch, the corrections one segmented
+ *     operation over rows sorted by adapter.
+ *   - "LoRA Adapters: Many Models in One", "The model runner's part": stacked
+ *     A/B tensors with one slot per active adapter and a per-token slot index
+ *     (or none); "Using it": every slot is allocated at the maximum rank and
+ *     smaller adapters are padded.
+ *   - "Adapter Residency When One Replica Serves Many Fine-Tunes", "What the
+ *     forward pass has to do differently": base projection dense over the
+ *     batch, each adapter applied to its rows only (a gather/scatter over row
+ *     indices); the scale belongs with the adapter.
+ *   - "S-LoRA: ...", "Unified paging": adapter weights held in fixed-size
+ *     blocks of one pool, found through a per-adapter block list.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors) unless a parameter says "host".  The caller owns every buffer;
+ *     the library never allocates or frees device memory inside these calls.
+ *   - Row-major layouts.  Leading dimensions are in elements.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Compute calls are asynchronous on it and never synchronise, except
+ *     lora_check and lora_profile_read, which say so.
+ *   - Errors are returned as lora_status_t; nothing throws across the ABI.
+ *     Argument errors are detected on the host before anything is launched.
+ *     Errors in DEVICE-resident arguments (ids, ranks, page-table entries)
+ *     are detected on the device: the offending rows are treated as having
+ *     no adapter, are counted, and lora_check reports the counts.
+ *   - One workspace must not be used by two calls in flight at once (e.g. on
+ *     two streams).
+ */
+#ifndef LORA_ROW_H
+#define LORA_ROW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+
+typedef enum lora_status {
+  LORA_OK = 0,
+  LORA_ERR_ARG = 1,         /* null pointer, bad enum, negative size, bad flag combination */
+  LORA_ERR_SHAPE = 2,       /* sizes / leading dims / alignment not supported */
+  LORA_ERR_DTYPE = 3,       /* unsupported dtype */
+  LORA_ERR_RANK = 4,        /* max_rank out of the supported range */
+  LORA_ERR_WORKSPACE = 5,   /* workspace too small or misaligned */
+  LORA_ERR_PAGE = 6,        /* pool geometry invalid (page size, counts) */
+  LORA_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
+  LORA_ERR_UNSUPPORTED = 8  /* valid request that this build does not implement */
+} lora_status_t;
+
+typedef enum lora_dtype {
+  LORA_DTYPE_F32 = 0,   /* x, W, A, B, y in fp32; true fp32 products, fp32 accumulation */
+  LORA_DTYPE_BF16 = 1   /* x, W, A, B, y in bf16; fp32 accumulation, RNE on store */
+} lora_dtype_t;
+
+typedef enum lora_path {
+  LORA_PATH_AUTO = 0,    /* choose by row count per adapter */
+  LORA_PATH_GATHER = 1,  /* decode-sized: per-row gather, VALU dot products, wavefront
+                            reduction over k, A staged in LDS */
+  LORA_PATH_SGMV = 2     /* prefill-sized runs of rows sharing an adapter: MFMA tiles over
+                            the adapter-sorted segments */
+} lora_path_t;
+
+/* Flags for lora_linear. */
+#define LORA_FLAG_REUSE_PLAN 1u  /* skip the plan step and use the plan already in the
+                                    workspace (made by lora_plan or an earlier lora_linear on
+                                    the same adapter_ids, M and adapter set).  One plan serves
+                                    every adapted layer of a step, since ids are per token. */
+
+/* Where adapter weights live. */
+typedef enum lora_adapter_kind {
+  LORA_ADAPTERS_SLOTS = 0,  /* stacked, rank-padded slots */
+  LORA_ADAPTERS_POOL = 1    /* unified pool of fixed-size pages + per-adapter page table */
+} lora_adapter_kind_t;
+
+/*
+ * Adapter set.  The struct itself is HOST memory (read during the call only);
+ * the arrays it points to are device memory.
+ *
+ * SLOTS: A [n_adapters, max_rank, k] and B [n_adapters, d, max_rank], same
+ *   dtype as x.  Slot s holds A_s in rows 0..r_s-1 of A[s] and B_s in columns
+ *   0..r_s-1 of B[s]; the kernels read only those (padding is never read and
+ *   may hold anything).
+ * POOL: `pool` is n_pages * page_bytes bytes.  Adapter a's logical byte space
+ *   is A_a (r_a x k, row-major) followed by B_a (d x r_a, row-major, row
+ *   stride r_a), both unpadded, in x's dtype; logical page j of it is physical
+ *   page page_table[a * max_pages + j] of the pool.  page_bytes is a power of
+ *   two >= 256.  Entries that an adapter does not need are ignored.
+ * ranks: device int32 [n_adapters], true rank r_s of each slot / adapter,
+ *   0 <= r_s <= max_rank (a rank outside that range is a device-side error).
+ */
+typedef struct lora_adapters {
+  int32_t kind;               /* lora_adapter_kind_t */
+  int32_t n_adapters;         /* S: number of slots (SLOTS) or adapters (POOL) */
+  int32_t max_rank;           /* R: 1..256; slot padding width (SLOTS), rank cap (both) */
+  int32_t max_pages;          /* POOL: columns of page_table */
+  const int32_t *ranks;       /* device int32 [S] */
+  const void *A;              /* SLOTS: device [S, R, k] */
+  const void *B;              /* SLOTS: device [S, d, R] */
+  const void *pool;           /* POOL: device bytes [n_pages * page_bytes] */
+  const int32_t *page_table;  /* POOL: device int32 [S, max_pages] */
+  int64_t page_bytes;         /* POOL */
+  int64_t n_pages;            /* POOL */
+} lora_adapters_t;
+
+/* ABI version of the loaded library (LORA_ABI_VERSION it was built with). */
+int32_t lora_abi_version(void);
+
+/* Static description of a status code. */
+const char *lora_status_str(lora_status_t status);
+
+/*
+ * Bytes of workspace lora_linear / lora_plan need for up to max_rows rows
+ * with this adapter set (covers every path).  Host-only; no device access.
+ * Returns 0 on invalid arguments.  The workspace is caller-owned device
+ * memory, 256-byte aligned; its contents need no initialisation.
+ */
+size_t lora_workspace_bytes(int64_t max_rows, int64_t d, int64_t k, lora_dtype_t dtype,
+                            const lora_adapters_t *adapters);
+
+/*
+ * Base projection only: y = x W^T.  Same kernels as the base step of
+ * lora_linear, so rows with no adapter there are bitwise equal to this.
+ * x [M, k] (ldx >= k), W [d, k] (ldw >= k), y [M, d] (ldy >= d).
+ * bf16: k, ldx, ldw multiples of 8 and ldy a multiple of 2; f32: k, ldx, ldw
+ * multiples of 4.  M == 0 is a no-op.
+ */
+lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
+                        int64_t ldx, const void *W, int64_t ldw, void *y, int64_t ldy,
+                        void *stream);
+
+/*
+ * The LoRA linear layer (see the top of this file).
+ *   adapter_ids: device int32 [M]; -1 = no adapter; other values outside
+ *                [0, n_adapters) are device-side errors (row treated as none).
+ *   scales:      device fp32 [n_adapters]; scale of slot / adapter s.
+ *   workspace:   device, >= lora_workspace_bytes(M, d, k, dtype, adapters).
+ *   path:        lora_path_t; flags: LORA_FLAG_* (0 for none).
+ * Steps, all on `stream`: plan (validate ids, stable sort of adapted rows
+ * by adapter, segment and work-item tables), base GEMM y = x W^T, shrink
+ * t = x A_s^T over k into fp32 partials, expand y += scale_s t B_s^T on
+ * adapted rows only.  Rows with no adapter are written once, by the GEMM.
+ * Results are run-to-run deterministic (no floating-point atomics).
+ */
+lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
+                          int64_t ldx, const void *W, int64_t ldw,
+                          const lora_adapters_t *adapters, const int32_t *adapter_ids,
+                          const float *scales, void *y, int64_t ldy, void *workspace,
+                          size_t workspace_bytes, int32_t path, uint32_t flags, void *stream);
+
+/*
+ * The plan step alone (what lora_linear runs first): classify rows, sort
+ * the adapted rows by (adapter, row) -- stable -- and build the segment
+ * table.  "Adapter Residency ...", "Batch composition under many adapters":
+ * rows sorted by adapter before the forward pass, each adapter's rows
+ * contiguous.  d and k are needed only to check page counts of a pool.
+ * M <= LORA_PLAN_MAX_ROWS.
+ */
+#define LORA_PLAN_MAX_ROWS 8192
+lora_status_t lora_plan(int64_t M, int64_t k, int64_t d, lora_dtype_t dtype,
+                        const lora_adapters_t *adapters, const int32_t *adapter_ids,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device pointers into a workspace holding a plan (no device access). */
+typedef struct lora_plan_view {
+  const int32_t *counters;     /* [0] bad ids [1] bad ranks [2] bad pages [3] n_adapted
+                                  [4] n_segments [5] gather items [6] sgmv items [7] rows */
+  const int32_t *perm;         /* [n_adapted]: adapted rows, sorted by (adapter, row) */
+  const int32_t *seg_adapter;  /* [n_segments], ascending */
+  const int32_t *seg_start;    /* [n_segments]: index into perm */
+  const int32_t *seg_len;      /* [n_segments] */
+  int64_t capacity_rows;       /* rows the view was laid out for */
+} lora_plan_view_t;
+
+lora_status_t lora_plan_view(const void *workspace, size_t workspace_bytes, int64_t M,
+                             const lora_adapters_t *adapters, lora_plan_view_t *out);
+
+/*
+ * Page-table translation as the kernels do it, exported for bit-exact checks:
+ * phys_off[i] = page_table[adapter[i]][logical_off[i] / page_bytes] * page_bytes
+ *               + logical_off[i] % page_bytes,
+ * or -1 when adapter[i] is outside [0, n_adapters), the logical page is past
+ * max_pages, or the entry is outside [0, n_pages).
+ * adapter, logical_off, phys_off: device arrays of n entries.  POOL only.
+ */
+lora_status_t lora_translate(const lora_adapters_t *adapters, const int32_t *adapter,
+                             const int64_t *logical_off, int64_t n, int64_t *phys_off,
+                             void *stream);
+
+/*
+ * Synchronises `stream` and reads the error counters of the last plan run in
+ * this workspace: rows with an id outside [-1, n_adapters), rows whose
+ * adapter rank is outside [0, max_rank], rows whose adapter pages are
+ * missing or outside the pool.  Output pointers are HOST and may be NULL.
+ */
+lora_status_t lora_check(const void *workspace, void *stream, int64_t *n_bad_ids,
+                         int64_t *n_bad_ranks, int64_t *n_bad_pages);
+
+/*
+ * Per-kernel GPU timing.  While enabled, every kernel that lora_linear /
+ * lora_gemm / lora_plan launches is bracketed by two hipEvents recorded on
+ * the launch stream; lora_profile_read synchronises on those events and
+ * accumulates elapsed time per kernel class.  Disabled by default.  The
+ * library creates its events once (lazily) and keeps them until unload.
+ */
+typedef enum lora_kernel_class {
+  LORA_K_PLAN = 0,
+  LORA_K_GEMM = 1,
+  LORA_K_SHRINK = 2,        /* gather-path shrink */
+  LORA_K_EXPAND = 3,        /* gather-path expand */
+  LORA_K_SGMV_SHRINK = 4,
+  LORA_K_SGMV_EXPAND = 5,
+  LORA_K_COUNT = 6
+} lora_kernel_class_t;
+
+typedef struct lora_profile {
+  double ms[LORA_K_COUNT];      /* summed kernel time per class */
+  int64_t launches[LORA_K_COUNT];
+  int64_t dropped;              /* launches not timed because the event ring was full */
+} lora_profile_t;
+
+lora_status_t lora_profile_enable(int32_t on);
+lora_status_t lora_profile_read(lora_profile_t *out, int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_ROW_H */

@@ -1,1 +1,13 @@
-"""Multi-adapter LoRA linear layer for AMD MI355X (gfx950)."""
+"""Multi-adapter LoRA linear layer for AMD MI355X (gfx950).
+
+The product is the C-ABI library ``liblora_row.so`` (HIP kernels for CDNA4),
+declared in ``include/lora_row.h``; this package is a thin ctypes binding
+with the same entry-point names.  The library is loaded on first use and its
+absence is an error: there is no fallback.
+"""
+from ._binding import (  # noqa: F401
+    FLAG_REUSE_PLAN, KERNEL_CLASSES, PATH_AUTO, PATH_GATHER, PATH_SGMV, PLAN_MAX_ROWS, Adapters,
+    LoraError, Profiler, abi_version, library_path, load_library, lora_check, lora_gemm,
+    lora_linear, lora_plan, lora_plan_view, lora_translate, new_workspace, status_str,
+    workspace_bytes,
+)

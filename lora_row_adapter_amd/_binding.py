@@ -1,0 +1,351 @@
+"""ctypes binding of liblora_row.so (declared in include/lora_row.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype and
+layout, and their device pointers, leading dimensions and the current HIP
+stream are handed to the C entry points of the same names.  Every step of
+the layer runs in the library's HIP kernels.  If the library is missing the
+call raises; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "liblora_row.so"
+
+PATH_AUTO, PATH_GATHER, PATH_SGMV = 0, 1, 2
+FLAG_REUSE_PLAN = 1
+KIND_SLOTS, KIND_POOL = 0, 1
+PLAN_MAX_ROWS = 8192
+KERNEL_CLASSES = ("plan", "gemm", "shrink", "expand", "sgmv_shrink", "sgmv_expand")
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_str(status), status))
+
+
+class _CAdapters(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("n_adapters", ctypes.c_int32),
+        ("max_rank", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("ranks", ctypes.c_void_p),
+        ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
+        ("pool", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("page_bytes", ctypes.c_int64),
+        ("n_pages", ctypes.c_int64),
+    ]
+
+
+class _CPlanView(ctypes.Structure):
+    _fields_ = [
+        ("counters", ctypes.c_void_p),
+        ("perm", ctypes.c_void_p),
+        ("seg_adapter", ctypes.c_void_p),
+        ("seg_start", ctypes.c_void_p),
+        ("seg_len", ctypes.c_void_p),
+        ("capacity_rows", ctypes.c_int64),
+    ]
+
+
+class _CProfile(ctypes.Structure):
+    _fields_ = [
+        ("ms", ctypes.c_double * 6),
+        ("launches", ctypes.c_int64 * 6),
+        ("dropped", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built; run `python -c 'import __graft_entry__ as g; g.build()'`"
+                           " (the HIP path has no fallback)" % path)
+    lib = ctypes.CDLL(path)
+    i32, i64, u32, p, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_size_t
+    pad = ctypes.POINTER(_CAdapters)
+    lib.lora_abi_version.argtypes = []
+    lib.lora_abi_version.restype = i32
+    lib.lora_status_str.argtypes = [i32]
+    lib.lora_status_str.restype = ctypes.c_char_p
+    lib.lora_workspace_bytes.argtypes = [i64, i64, i64, i32, pad]
+    lib.lora_workspace_bytes.restype = sz
+    lib.lora_gemm.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.lora_gemm.restype = i32
+    lib.lora_linear.argtypes = [i32, i64, i64, i64, p, i64, p, i64, pad, p, p, p, i64, p, sz, i32,
+                                u32, p]
+    lib.lora_linear.restype = i32
+    lib.lora_plan.argtypes = [i64, i64, i64, i32, pad, p, p, sz, p]
+    lib.lora_plan.restype = i32
+    lib.lora_plan_view.argtypes = [p, sz, i64, pad, ctypes.POINTER(_CPlanView)]
+    lib.lora_plan_view.restype = i32
+    lib.lora_translate.argtypes = [pad, p, p, i64, p, p]
+    lib.lora_translate.restype = i32
+    lib.lora_check.argtypes = [p, p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.lora_check.restype = i32
+    lib.lora_profile_enable.argtypes = [i32]
+    lib.lora_profile_enable.restype = i32
+    lib.lora_profile_read.argtypes = [ctypes.POINTER(_CProfile), i32]
+    lib.lora_profile_read.restype = i32
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().lora_abi_version())
+
+
+def status_str(status: int) -> str:
+    try:
+        return load_library().lora_status_str(int(status)).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "status %d" % status
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise LoraError(status, what)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+    return _DTYPES[t.dtype]
+
+
+def _rows(t: torch.Tensor, name: str):
+    """(pointer, leading dimension) of a row-major 2-D device tensor."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.stride(1) != 1:
+        raise ValueError("%s must have unit stride along its last dimension" % name)
+    return t.data_ptr(), t.stride(0)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s" % (name, dtype))
+    return t.data_ptr()
+
+
+class Adapters:
+    """An adapter set: stacked rank-padded slots or a paged pool.
+
+    Holds references to the device tensors so they outlive the descriptor."""
+
+    def __init__(self, kind: int, ranks: torch.Tensor, max_rank: int, A=None, B=None, pool=None,
+                 page_table=None, page_bytes: int = 0, n_pages: int = 0):
+        self.kind = kind
+        self.ranks = ranks
+        self.max_rank = int(max_rank)
+        self.A, self.B, self.pool, self.page_table = A, B, pool, page_table
+        self.page_bytes = int(page_bytes)
+        self.n_pages = int(n_pages)
+        self.n_adapters = int(ranks.numel())
+        c = _CAdapters()
+        c.kind = kind
+        c.n_adapters = self.n_adapters
+        c.max_rank = self.max_rank
+        c.ranks = _dev(ranks, "ranks", torch.int32)
+        if kind == KIND_SLOTS:
+            c.A = _dev(A, "A")
+            c.B = _dev(B, "B")
+        else:
+            if page_table.dim() != 2 or page_table.shape[0] != self.n_adapters:
+                raise ValueError("page_table must be [n_adapters, max_pages]")
+            c.pool = _dev(pool, "pool")
+            c.page_table = _dev(page_table, "page_table", torch.int32)
+            c.max_pages = int(page_table.shape[1])
+            c.page_bytes = self.page_bytes
+            c.n_pages = self.n_pages
+        self._c = c
+
+    @classmethod
+    def slots(cls, A: torch.Tensor, B: torch.Tensor, ranks: torch.Tensor) -> "Adapters":
+        """A [S, R, k], B [S, d, R], ranks int32 [S] (device)."""
+        if A.dim() != 3 or B.dim() != 3 or A.shape[0] != B.shape[0] or A.shape[1] != B.shape[2]:
+            raise ValueError("slots must be A [S, R, k] and B [S, d, R]")
+        if A.dtype != B.dtype:
+            raise TypeError("A and B differ in dtype")
+        return cls(KIND_SLOTS, ranks, A.shape[1], A=A, B=B)
+
+    @classmethod
+    def paged(cls, pool: torch.Tensor, page_table: torch.Tensor, ranks: torch.Tensor,
+              page_bytes: int, max_rank: int) -> "Adapters":
+        """pool: device bytes [n_pages * page_bytes]; page_table int32 [S, max_pages]."""
+        if pool.numel() * pool.element_size() % page_bytes:
+            raise ValueError("pool size is not a whole number of pages")
+        n_pages = pool.numel() * pool.element_size() // page_bytes
+        return cls(KIND_POOL, ranks, max_rank, pool=pool, page_table=page_table,
+                   page_bytes=page_bytes, n_pages=n_pages)
+
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def workspace_bytes(max_rows: int, d: int, k: int, dtype: torch.dtype, adapters: Adapters) -> int:
+    n = load_library().lora_workspace_bytes(int(max_rows), int(d), int(k), _DTYPES[dtype], adapters.ref())
+    if n == 0:
+        raise LoraError(1, "lora_workspace_bytes")
+    return int(n)
+
+
+def new_workspace(max_rows: int, d: int, k: int, dtype: torch.dtype, adapters: Adapters,
+                  device=None) -> torch.Tensor:
+    n = workspace_bytes(max_rows, d, k, dtype, adapters)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def lora_gemm(x: torch.Tensor, W: torch.Tensor, y: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """y = x W^T on the device (base projection only)."""
+    lib = load_library()
+    if y is None:
+        y = torch.empty((x.shape[0], W.shape[0]), dtype=x.dtype, device=x.device)
+    xp, ldx = _rows(x, "x")
+    wp, ldw = _rows(W, "W")
+    yp, ldy = _rows(y, "y")
+    if W.dtype != x.dtype or y.dtype != x.dtype:
+        raise TypeError("x, W, y must share a dtype")
+    _check(lib.lora_gemm(_dtype_code(x), x.shape[0], x.shape[1], W.shape[0], xp, ldx, wp, ldw,
+                         yp, ldy, _stream_ptr(stream)), "lora_gemm")
+    return y
+
+
+def lora_linear(x: torch.Tensor, W: torch.Tensor, adapters: Adapters, adapter_ids: torch.Tensor,
+                scales: torch.Tensor, y: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, path: int = PATH_AUTO, flags: int = 0,
+                stream=None) -> torch.Tensor:
+    """y = x W^T + scale_s (x A_s^T) B_s^T per row (s = adapter_ids[m], -1 = none)."""
+    lib = load_library()
+    M, k = x.shape
+    d = W.shape[0]
+    if y is None:
+        y = torch.empty((M, d), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(M, d, k, x.dtype, adapters, device=x.device)
+    xp, ldx = _rows(x, "x")
+    wp, ldw = _rows(W, "W")
+    yp, ldy = _rows(y, "y")
+    if W.dtype != x.dtype or y.dtype != x.dtype:
+        raise TypeError("x, W, y must share a dtype")
+    if adapters.kind == KIND_SLOTS and adapters.A.dtype != x.dtype:
+        raise TypeError("adapter slots must have x's dtype")
+    if adapter_ids.numel() != M:
+        raise ValueError("adapter_ids must have one entry per row")
+    st = lib.lora_linear(_dtype_code(x), M, k, d, xp, ldx, wp, ldw, adapters.ref(),
+                         _dev(adapter_ids, "adapter_ids", torch.int32),
+                         _dev(scales, "scales", torch.float32), yp, ldy,
+                         _dev(workspace, "workspace"), workspace.numel(), int(path), int(flags),
+                         _stream_ptr(stream))
+    _check(st, "lora_linear")
+    return y
+
+
+def lora_plan(adapter_ids: torch.Tensor, adapters: Adapters, k: int, d: int, dtype: torch.dtype,
+              workspace: torch.Tensor, stream=None) -> None:
+    lib = load_library()
+    _check(lib.lora_plan(adapter_ids.numel(), int(k), int(d), _DTYPES[dtype], adapters.ref(),
+                         _dev(adapter_ids, "adapter_ids", torch.int32), _dev(workspace, "workspace"),
+                         workspace.numel(), _stream_ptr(stream)), "lora_plan")
+
+
+def lora_plan_view(workspace: torch.Tensor, M: int, adapters: Adapters) -> dict:
+    """Copies of the plan arrays in the workspace (synchronises)."""
+    lib = load_library()
+    v = _CPlanView()
+    _check(lib.lora_plan_view(_dev(workspace, "workspace"), workspace.numel(), int(M), adapters.ref(),
+                              ctypes.byref(v)), "lora_plan_view")
+    base = workspace.data_ptr()
+
+    def arr(ptr, n):
+        off = int(ptr) - base
+        return workspace[off:off + 4 * n].view(torch.int32).cpu().numpy().copy()
+
+    counters = arr(v.counters, 8)
+    n_ad, n_seg = int(counters[3]), int(counters[4])
+    return {
+        "n_bad_ids": int(counters[0]), "n_bad_ranks": int(counters[1]),
+        "n_bad_pages": int(counters[2]), "n_adapted": n_ad, "n_segments": n_seg,
+        "items_gather": int(counters[5]), "items_sgmv": int(counters[6]), "rows": int(counters[7]),
+        "perm": arr(v.perm, n_ad), "seg_adapter": arr(v.seg_adapter, n_seg),
+        "seg_start": arr(v.seg_start, n_seg), "seg_len": arr(v.seg_len, n_seg),
+    }
+
+
+def lora_translate(adapters: Adapters, adapter: torch.Tensor, logical_off: torch.Tensor,
+                   stream=None) -> torch.Tensor:
+    lib = load_library()
+    n = adapter.numel()
+    if logical_off.numel() != n:
+        raise ValueError("adapter and logical_off differ in length")
+    out = torch.empty(n, dtype=torch.int64, device=adapter.device)
+    _check(lib.lora_translate(adapters.ref(), _dev(adapter, "adapter", torch.int32),
+                              _dev(logical_off, "logical_off", torch.int64), n,
+                              _dev(out, "phys_off"), _stream_ptr(stream)), "lora_translate")
+    return out
+
+
+def lora_check(workspace: torch.Tensor, stream=None) -> dict:
+    lib = load_library()
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.lora_check(_dev(workspace, "workspace"), _stream_ptr(stream), ctypes.byref(a),
+                          ctypes.byref(b), ctypes.byref(c)), "lora_check")
+    return {"n_bad_ids": a.value, "n_bad_ranks": b.value, "n_bad_pages": c.value}
+
+
+class Profiler:
+    """Per-kernel GPU time from events the library records around each launch."""
+
+    def __enter__(self):
+        lib = load_library()
+        _check(lib.lora_profile_read(None, 1), "lora_profile_read")
+        _check(lib.lora_profile_enable(1), "lora_profile_enable")
+        return self
+
+    def __exit__(self, *exc):
+        load_library().lora_profile_enable(0)
+        return False
+
+    @staticmethod
+    def read(reset: bool = False) -> dict:
+        p = _CProfile()
+        _check(load_library().lora_profile_read(ctypes.byref(p), int(reset)), "lora_profile_read")
+        return {name: {"ms": p.ms[i], "launches": p.launches[i]}
+                for i, name in enumerate(KERNEL_CLASSES)} | {"dropped": p.dropped}

@@ -1,0 +1,99 @@
+// common.hpp -- device-side types and helpers shared by the HIP kernels of
+// liblora_row (gfx950).  Internal; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+// ---------------------------------------------------------------------------
+// Tunables fixed at build time (the host lays out workspaces with them).
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxRows = 8192;  // LORA_PLAN_MAX_ROWS
+constexpr int kRowsPerGatherItem = 16;  // rows per shrink/expand work item (gather path)
+constexpr int kRowsPerSgmvItem = 64;    // rows per work item (SGMV path)
+constexpr int kMaxKSplit = 16;          // k-splits of the shrink (fp32 partials)
+constexpr int kMaxRank = 256;
+
+// Header words at the start of a workspace (int32).
+enum HdrWord {
+  kHdrBadIds = 0,
+  kHdrBadRanks = 1,
+  kHdrBadPages = 2,
+  kHdrAdapted = 3,
+  kHdrSegments = 4,
+  kHdrItemsGather = 5,
+  kHdrItemsSgmv = 6,
+  kHdrRows = 7,
+  kHdrWords = 64
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 <-> fp32.  bf16 is the upper half of an fp32; widening is exact.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// Round-to-nearest-even narrowing (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+// Work item of the LoRA kernels: `nrows` consecutive entries of the sorted
+// row permutation starting at `pos`, all using adapter `adapter` of rank `rank`.
+struct Item {
+  int32_t adapter;
+  int32_t pos;
+  int32_t nrows;
+  int32_t rank;
+};
+
+// Where one adapter's A and B live.  SLOTS: A [S, R, k] and B [S, d, R];
+// POOL: logical space [A r x k | B d x r] cut into pages.
+struct AdapterRef {
+  const uint8_t *A;        // SLOTS
+  const uint8_t *B;        // SLOTS
+  const uint8_t *pool;     // POOL
+  const int32_t *page_table;
+  int64_t page_bytes;
+  int32_t page_shift;
+  int32_t max_pages;
+  int32_t max_rank;
+  int32_t pooled;
+  int64_t k;
+  int64_t d;
+  int32_t elem_bytes;
+};
+
+// Byte address of A_s[j][kk] (a vector starting there never crosses a page
+// as long as it is aligned to its own size and the page size is a multiple).
+__device__ __forceinline__ const uint8_t *adapter_a_ptr(const AdapterRef &ar, int s, int r,
+                                                        int64_t j, int64_t kk) {
+  if (!ar.pooled) {
+    return ar.A + (((int64_t)s * ar.max_rank + j) * ar.k + kk) * ar.elem_bytes;
+  }
+  int64_t off = (j * ar.k + kk) * ar.elem_bytes;
+  int64_t page = ar.page_table[(int64_t)s * ar.max_pages + (off >> ar.page_shift)];
+  return ar.pool + (page << ar.page_shift) + (off & (ar.page_bytes - 1));
+}
+
+// Byte address of B_s[n][j].
+__device__ __forceinline__ const uint8_t *adapter_b_ptr(const AdapterRef &ar, int s, int r,
+                                                        int64_t n, int64_t j) {
+  if (!ar.pooled) {
+    return ar.B + (((int64_t)s * ar.d + n) * ar.max_rank + j) * ar.elem_bytes;
+  }
+  int64_t off = ((int64_t)r * ar.k + n * r + j) * ar.elem_bytes;
+  int64_t page = ar.page_table[(int64_t)s * ar.max_pages + (off >> ar.page_shift)];
+  return ar.pool + (page << ar.page_shift) + (off & (ar.page_bytes - 1));
+}
+
+}  // namespace lora

@@ -1,0 +1,68 @@
+// kernels.hpp -- host-side launchers of the HIP kernels (internal to liblora_row).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace lora {
+
+// Byte offsets of the workspace regions, laid out for `rows` rows (<= the
+// plan limit), S adapters and max rank R.  Every region is 256-byte aligned.
+struct WsLayout {
+  int64_t rows = 0;
+  int64_t seg_cap = 0;
+  int64_t items_g_cap = 0;
+  int64_t items_s_cap = 0;
+  int32_t R = 0;
+  size_t hdr = 0, perm = 0, seg_adapter = 0, seg_start = 0, seg_len = 0;
+  size_t items_g = 0, items_s = 0, tpart = 0, total = 0;
+};
+WsLayout ws_layout(int64_t rows, int32_t S, int32_t R);
+
+struct PlanArgs {
+  const int32_t *ids;
+  const int32_t *ranks;
+  int32_t M;
+  int32_t S;
+  int32_t R;
+  int32_t row_bits;  // log2 of the sort width
+  // pool checks (page_table == nullptr for slots)
+  const int32_t *page_table;
+  int32_t max_pages;
+  int64_t n_pages;
+  int64_t page_bytes;
+  int64_t bytes_per_rank;  // (k + d) * elem_bytes
+  // outputs
+  uint8_t *ws;
+  WsLayout L;
+};
+
+struct LoraArgs {
+  int32_t dtype;  // 0 f32, 1 bf16
+  int64_t k, d;
+  const void *x;
+  int64_t ldx;
+  void *y;
+  int64_t ldy;
+  const float *scales;
+  AdapterRef ar;
+  uint8_t *ws;
+  WsLayout L;
+  int32_t ksplit;
+  int64_t kchunk;  // k per split (multiple of 256)
+};
+
+hipError_t launch_plan(const PlanArgs &a, hipStream_t st);
+hipError_t launch_translate(const AdapterRef &ar, int32_t S, int64_t n_pages,
+                            const int32_t *adapter, const int64_t *off, int64_t n,
+                            int64_t *phys, hipStream_t st);
+hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
+                       const void *W, int64_t ldw, void *y, int64_t ldy, hipStream_t st);
+hipError_t launch_shrink_gather(const LoraArgs &a, hipStream_t st);
+hipError_t launch_expand_gather(const LoraArgs &a, hipStream_t st);
+hipError_t launch_shrink_sgmv(const LoraArgs &a, hipStream_t st);
+hipError_t launch_expand_sgmv(const LoraArgs &a, hipStream_t st);
+
+}  // namespace lora

@@ -257,16 +257,19 @@ def make(name: str, **kw) -> Workload:
 # ----------------------------------------------------------------------------
 
 def slots(w: Workload, proj: Projection, R: Optional[int] = None, pad_value: float = 0.0):
-    """Stacked, rank-padded slots: A_slots [S, R, k], B_slots [S, d, R]."""
+    """Stacked, rank-padded slots: A_slots [S, R, k], B_slots [S, d, R].
+
+    An adapter whose rank exceeds R (an invalid set, for error tests) keeps
+    only its first R rows here."""
     R = w.max_rank if R is None else R
     S, k, d = w.S, w.k, proj.d
     A = torch.full((S, R, k), pad_value, dtype=w.dtype)
     B = torch.full((S, d, R), pad_value, dtype=w.dtype)
     for s in range(S):
-        r = int(w.ranks[s])
+        r = min(int(w.ranks[s]), R)
         if r:
-            A[s, :r, :] = proj.A[s]
-            B[s, :, :r] = proj.B[s]
+            A[s, :r, :] = proj.A[s][:r]
+            B[s, :, :r] = proj.B[s][:, :r]
     return A.contiguous(), B.contiguous()
 
 
