@@ -1,0 +1,234 @@
+"""Benchmark: multi-adapter LoRA linear on one MI355X.
+
+One step = the whole hot path over one decode batch of the 70B-shaped
+projections: plan (once, shared by both projections) + q (8192 -> 8192) and
+v (8192 -> 1024) LoRA linear layers, each = base GEMM + shrink + expand, for
+512 rows with 12 adapters of rank {4 x3, 16 x6, 64 x3} (alpha = 2r, Zipf 1.1
+popularity, 10% rows without adapter), bf16 with fp32 accumulation.
+
+Inputs are seeded synthetic tensors already resident in HBM.  The step
+rotates over several independent buffer sets (x, W_q, W_v, adapter slots,
+outputs; ~1.6 GB total), so weights are not served from the 256 MiB
+Infinity Cache between steps.
+
+Prints one JSON line (rank 0):
+  value      = tokens/s through the (q + v) pair = 512 * steps / elapsed
+  roofline   = base GEMM (the dominant kernel) MFMA TFLOP/s vs the bf16 peak,
+               from per-launch HIP events recorded on the launch stream
+  cpu_baseline = the fp64 oracle on a bounded row sample, on the host cores
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c3_gemm.json")
+GEMM_SOURCE = os.path.join(ROOT, "lora_row_adapter_amd", "csrc", "gemm.hip")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets")
+    ap.add_argument("--path", default="auto", choices=["auto", "gather", "sgmv"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer is row-independent and this build runs on a "
+              "single MI355X (--gpus %d requested); see DESIGN.md for how it would shard."
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import lora_row_adapter_amd as lr
+    from lora_row_adapter_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    lr.load_library()
+    path = {"auto": lr.PATH_AUTO, "gather": lr.PATH_GATHER, "sgmv": lr.PATH_SGMV}[args.path]
+
+    log("generating c3_proj70b_bf16")
+    w = wl.c3_proj70b_bf16()
+    M, k = w.M, w.k
+    pq, pv = w.proj("q"), w.proj("v")
+    ids = torch.from_numpy(w.ids).to(dev)
+    scales = torch.from_numpy(w.scales).to(dev)
+    ranks = torch.from_numpy(w.ranks).to(dev)
+
+    def slot_adapters(p):
+        A, B = wl.slots(w, p)
+        return A.to(dev), B.to(dev)
+
+    base = {"x": w.x.to(dev), "Wq": pq.W.to(dev), "Wv": pv.W.to(dev)}
+    base["Aq"], base["Bq"] = slot_adapters(pq)
+    base["Av"], base["Bv"] = slot_adapters(pv)
+    sets = []
+    for i in range(args.sets):
+        s = {kk: (v if i == 0 else v.clone()) for kk, v in base.items()}
+        s["adq"] = lr.Adapters.slots(s["Aq"], s["Bq"], ranks)
+        s["adv"] = lr.Adapters.slots(s["Av"], s["Bv"], ranks)
+        s["yq"] = torch.empty(M, pq.d, dtype=torch.bfloat16, device=dev)
+        s["yv"] = torch.empty(M, pv.d, dtype=torch.bfloat16, device=dev)
+        sets.append(s)
+    set_bytes = sum(v.numel() * v.element_size() for kk, v in sets[0].items() if torch.is_tensor(v))
+    ws = lr.new_workspace(M, max(pq.d, pv.d), k, torch.bfloat16, sets[0]["adq"], device=dev)
+    torch.cuda.synchronize()
+    log("%d buffer sets of %.0f MB" % (args.sets, set_bytes / 1e6))
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s = sets[i % len(sets)]
+        lr.lora_linear(s["x"], s["Wq"], s["adq"], ids, scales, y=s["yq"], workspace=ws, path=path,
+                       stream=stream)
+        lr.lora_linear(s["x"], s["Wv"], s["adv"], ids, scales, y=s["yv"], workspace=ws, path=path,
+                       flags=lr.FLAG_REUSE_PLAN, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = M * args.steps / elapsed
+    log("timed: %.3f ms/step, %.3g tokens/s" % (ms_per_step, value))
+
+    # the same steps again with per-launch events (library-side, on the
+    # launch stream) for per-kernel durations
+    with lr.Profiler():
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        prof = lr.Profiler.read(reset=True)
+        torch.cuda.synchronize()
+        ev_elapsed = time.perf_counter() - t1
+    per = {kname: prof[kname]["ms"] * 1e3 / max(prof[kname]["launches"], 1)
+           for kname in lr.KERNEL_CLASSES}
+    launches = {kname: prof[kname]["launches"] for kname in lr.KERNEL_CLASSES}
+    log("per-launch us: " + json.dumps({k_: round(v, 2) for k_, v in per.items()}))
+
+    bq = wl.algorithmic_bytes(w, pq)
+    bv = wl.algorithmic_bytes(w, pv)
+    gemm_flops = bq["gemm_flops"] + bv["gemm_flops"]
+    gemm_us_step = prof["gemm"]["ms"] * 1e3 / args.steps
+    gemm_tflops = gemm_flops / (gemm_us_step * 1e-6) / 1e12
+    shrink_us_step = (prof["shrink"]["ms"] + prof["sgmv_shrink"]["ms"]) * 1e3 / args.steps
+    expand_us_step = (prof["expand"]["ms"] + prof["sgmv_expand"]["ms"]) * 1e3 / args.steps
+    shrink_gbs = (bq["shrink_bytes"] + bv["shrink_bytes"]) / (shrink_us_step * 1e-6) / 1e9
+    expand_gbs = (bq["expand_bytes"] + bv["expand_bytes"]) / (expand_us_step * 1e-6) / 1e9
+    kernel_us_step = sum(prof[kname]["ms"] for kname in lr.KERNEL_CLASSES) * 1e3 / args.steps
+
+    traffic = None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+        src_sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        if t.get("source_sha256") == src_sha:
+            traffic = t["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+
+    result = {
+        "metric": "LoRA-linear tokens/s; shrink/expand HBM GB/s and base-GEMM TFLOP/s vs peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "c3_proj70b_bf16: q 8192->8192 and v 8192->1024 LoRA linear, 512 decode "
+                        "rows, 12 adapters ranks 4x3/16x6/64x3 alpha=2r, Zipf(1.1), 10% none",
+            "M": M, "k": k, "d_q": pq.d, "d_v": pv.d, "n_adapters": w.S, "max_rank": w.max_rank,
+            "adapter_storage": "slots", "path": args.path, "buffer_sets": args.sets,
+            "buffer_set_mb": round(set_bytes / 1e6, 1),
+        },
+        "roofline": {
+            "kernel": "k_gemm_bf16 (base GEMM, q and v launches)",
+            "bound": "mfma",
+            "achieved": gemm_tflops,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / BF16_PEAK_TFLOPS,
+            "traffic": traffic,
+        },
+        "kernels": {
+            "per_launch_us": {k_: round(v, 3) for k_, v in per.items() if launches[k_]},
+            "launches_per_step": {k_: launches[k_] / args.steps for k_ in launches if launches[k_]},
+            "kernel_us_per_step": round(kernel_us_step, 3),
+            "event_pass_ms_per_step": round(ev_elapsed * 1e3 / args.steps, 4),
+            "tokens_per_s_from_kernel_sum": M / (kernel_us_step * 1e-6),
+            "gemm_tflops": round(gemm_tflops, 1),
+            "shrink_gbs": round(shrink_gbs, 1),
+            "shrink_frac_hbm": round(shrink_gbs / HBM_PEAK_GBS, 4),
+            "expand_gbs": round(expand_gbs, 1),
+            "expand_frac_hbm": round(expand_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic": {"q": bq, "v": bv},
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, pq, pv, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, pq, pv, target_s):
+    """The fp64 oracle, as it is, on a bounded sample of the same rows."""
+    import oracle
+    threads = oracle.default_threads()
+    used = oracle.threads_used(threads)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.M)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        for p in (pq, pv):
+            oracle.lora_linear(w.x[torch.from_numpy(rows)], p.W, p.A, p.B,
+                               w.scales.astype(np.float64), w.ids[rows], max_rank=w.max_rank,
+                               n_threads=threads)
+        return time.perf_counter() - t0
+
+    probe = np.sort(order[:used])
+    t_probe = run(probe)
+    n = int(min(w.M, max(used, round(target_s / max(t_probe, 1e-9) * len(probe)))))
+    rows = np.sort(order[:n])
+    t = run(rows) if n != len(probe) else t_probe
+    log("cpu oracle: %d rows in %.1f s on %d threads" % (n, t, used))
+    return {"value": n / t, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "%d of the 512 rows (seeded), q and v projections, fp64, %.1f s" % (n, t)}
+
+
+if __name__ == "__main__":
+    main()

@@ -136,6 +136,200 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(int M, int N, int K, const ui
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined bf16 GEMM (K a multiple of 64, 16-byte aligned rows).
+//
+// Operand tiles go straight from HBM/L2 into LDS with buffer_load ... lds
+// (each lane's 16 bytes land at LDS base + 16 * lane; lanes past the end of
+// the buffer write zeros, which pads the M / N tails).  STAGES k-tiles are in
+// flight at once in a ring of LDS buffers, so load latency is hidden behind
+// the MFMAs of the tiles already resident.  Rows of a tile are 64 bf16 =
+// 8 chunks of 16 bytes, stored with chunk c of row r at position c ^ (r & 7)
+// so the 16 lanes that read one fragment column hit distinct banks.
+//
+// Tile BM x BN per 256-thread workgroup; WM x WN waves, each owning
+// (BM / WM) x (BN / WN) outputs as 16 x 16 MFMA blocks.
+// ---------------------------------------------------------------------------
+struct PipeArgs {
+  int M, N, K;
+  const uint16_t *x;
+  int64_t ldx;
+  const uint16_t *W;
+  int64_t ldw;
+  uint16_t *y;
+  int64_t ldy;
+  int tiles_m, tiles_n;
+  int vec_store;  // y rows 16-byte aligned (ldy % 8 == 0, aligned base)
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One 16-byte-per-lane load from global memory straight into LDS:
+// lane l's bytes at [base + voff, +16) land at lds + 16 * l; lanes with
+// voff + 16 > nbytes write zeros.  (Kept out of the kernel templates: the
+// buffer-resource type exists only in device compilation.)
+__device__ __forceinline__ void load16_to_lds(const void *base, uint32_t nbytes, void *lds,
+                                              uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(256) void k_gemm_bf16_pipe(PipeArgs p) {
+  constexpr int BKB = 128;                               // bytes per tile row (64 bf16)
+  constexpr int BROWS = ((BN + 31) / 32) * 32;           // B rows loaded (multiple of 32)
+  constexpr int A_INSTR = BM * 8 / 256;                  // 16-byte loads per thread per k-tile
+  constexpr int B_INSTR = BROWS * 8 / 256;
+  constexpr int LOADS = A_INSTR + B_INSTR;
+  constexpr int A_BYTES = BM * BKB;
+  constexpr int STAGE_BYTES = (BM + BROWS) * BKB;
+  constexpr int FM = BM / WM / 16;
+  constexpr int FN = BN / WN / 16;
+  constexpr int CLD = BN + 8;                            // epilogue LDS row (bf16)
+  static_assert(WM * WN == 4, "4 waves");
+  static_assert(FM * WM * 16 == BM && FN * WN * 16 == BN, "tile split");
+  constexpr int ECH = (STAGES * STAGE_BYTES >= BM * CLD * 2) ? BM : BM / 2;  // epilogue rows per pass
+  static_assert(STAGES * STAGE_BYTES >= ECH * CLD * 2, "epilogue fits");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+
+  const int nblk = p.tiles_m * p.tiles_n;
+  const int b = blockIdx.x;
+  const int t = ((nblk & 7) == 0) ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int tm = t % p.tiles_m;
+  const int tn = t / p.tiles_m;
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  const uint32_t a_bytes = (uint32_t)(min(BM, p.M - m0) * p.ldx * 2);
+  const uint32_t b_bytes = (uint32_t)(min(BN, p.N - n0) * p.ldw * 2);
+  const uint16_t *xa = p.x + (int64_t)m0 * p.ldx;
+  const uint16_t *wb = p.W + (int64_t)n0 * p.ldw;
+
+  // Per-thread source offsets (k-tile 0).  Load i of wave w fills LDS
+  // chunks (w * INSTR + i) * 64 + lane of its operand region.
+  uint32_t va[A_INSTR], vb[B_INSTR];
+#pragma unroll
+  for (int i = 0; i < A_INSTR; ++i) {
+    const int P = (wave * A_INSTR + i) * 64 + lane;
+    const int row = P >> 3;
+    const int c = (P & 7) ^ (row & 7);
+    va[i] = (uint32_t)(row * p.ldx * 2 + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < B_INSTR; ++i) {
+    const int P = (wave * B_INSTR + i) * 64 + lane;
+    const int row = P >> 3;
+    const int c = (P & 7) ^ (row & 7);
+    // rows past BN (padding of the load pattern) read past the buffer: zeros
+    vb[i] = row < BN ? (uint32_t)(row * p.ldw * 2 + c * 16) : 0xFFFFFFF0u;
+  }
+
+  const int nk = p.K / 64;
+  auto issue = [&](int kt, int stage) {
+    uint8_t *sa = smem + stage * STAGE_BYTES;
+    uint8_t *sb = sa + A_BYTES;
+    const uint32_t kb = (uint32_t)kt * BKB;
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i)
+      load16_to_lds(xa, a_bytes, sa + (wave * A_INSTR + i) * 1024, va[i] + kb);
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i)
+      load16_to_lds(wb, b_bytes, sb + (wave * B_INSTR + i) * 1024,
+                    vb[i] == 0xFFFFFFF0u ? vb[i] : vb[i] + kb);
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int wm0 = (wave / WN) * (FM * 16);
+  const int wn0 = (wave % WN) * (FN * 16);
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int rem = min(STAGES - 2, nk - 1 - kt);
+    if (rem >= 2) wait_vmcnt<2 * LOADS>();
+    else if (rem == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    // Raw barrier: this wave's loads of tile kt are complete (vmcnt above);
+    // after the barrier every wave's are, and every wave has finished reading
+    // the stage that the next issue overwrites.  (A fenced barrier would wait
+    // for all loads in flight, including the tiles still streaming in.)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const uint8_t *sa = smem + (kt % STAGES) * STAGE_BYTES;
+    const uint8_t *sb = sa + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int pc = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t *>(sa + (wm0 + i * 16 + (lane & 15)) * BKB + pc);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + (wn0 + j * 16 + (lane & 15)) * BKB + pc);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // epilogue: bf16 tile through LDS (ECH rows per pass), then 16-byte row stores
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  uint16_t *ct = reinterpret_cast<uint16_t *>(smem);
+#pragma unroll
+  for (int r0 = 0; r0 < BM; r0 += ECH) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rb = wm0 + i * 16;
+      if (rb < r0 || rb >= r0 + ECH) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          ct[(rb - r0 + ((lane >> 4) << 2) + e) * CLD + wn0 + j * 16 + (lane & 15)] =
+              f32_to_bf16_bits(acc[i][j][e]);
+    }
+    __syncthreads();
+    for (int ch = tid; ch < ECH * CPR; ch += 256) {
+      const int row = ch / CPR;
+      const int c = ch - row * CPR;
+      const int gm = m0 + r0 + row;
+      const int gn = n0 + c * 8;
+      if (gm >= p.M || gn >= p.N) continue;
+      const uint16_t *src = ct + row * CLD + c * 8;
+      uint16_t *dst = p.y + (int64_t)gm * p.ldy + gn;
+      if (p.vec_store && gn + 8 <= p.N) {
+        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+      } else {
+        for (int e = 0; e < 8 && gn + e < p.N; ++e) dst[e] = src[e];
+      }
+    }
+  }
+}
+
 constexpr int FBM = 64, FBN = 64, FBK = 16;
 
 __global__ __launch_bounds__(256) void k_gemm_f32(int M, int N, int K, const float *__restrict__ x,
@@ -188,12 +382,63 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int M, int N, int K, const flo
   }
 }
 
+template <int BM, int BN, int WM, int WN, int STAGES>
+void launch_pipe(const PipeArgs &pa0, hipStream_t st) {
+  PipeArgs pa = pa0;
+  pa.tiles_m = (pa.M + BM - 1) / BM;
+  pa.tiles_n = (pa.N + BN - 1) / BN;
+  hipLaunchKernelGGL((k_gemm_bf16_pipe<BM, BN, WM, WN, STAGES>), dim3(pa.tiles_m * pa.tiles_n),
+                     dim3(256), 0, st, pa);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, hipStream_t st) {
   if (M <= 0 || d <= 0) return hipSuccess;
   if (dtype == 1) {
+    const bool pipe_ok = (k % 64) == 0 && (uint64_t)256 * ldx * 2 < (1ull << 32) &&
+                         (uint64_t)256 * ldw * 2 < (1ull << 32);
+    if (pipe_ok) {
+      PipeArgs pa{};
+      pa.M = (int)M;
+      pa.N = (int)d;
+      pa.K = (int)k;
+      pa.x = (const uint16_t *)x;
+      pa.ldx = ldx;
+      pa.W = (const uint16_t *)W;
+      pa.ldw = ldw;
+      pa.y = (uint16_t *)y;
+      pa.ldy = ldy;
+      pa.vec_store = ((ldy % 8) == 0 && ((uintptr_t)y & 15) == 0) ? 1 : 0;
+      // Tile choice: fill the 256 CUs with as few, as large tiles as
+      // possible.  Relative per-FLOP costs of the shapes were measured on
+      // MI355X (bigger tiles move fewer bytes per FLOP into LDS).
+      struct Cand { int bm, bn; double cost; };
+      const Cand cands[] = {{256, 256, 0.87}, {256, 128, 0.90}, {128, 144, 0.97},
+                            {128, 128, 1.00}, {64, 64, 2.2}};
+      int best = 3;
+      double best_t = 1e30;
+      for (int c = 0; c < 5; ++c) {
+        const Cand &cd = cands[c];
+        if (cd.bn == 144 && d % 144 != 0) continue;
+        const int64_t tiles = ((M + cd.bm - 1) / cd.bm) * ((d + cd.bn - 1) / cd.bn);
+        const int64_t rounds = (tiles + 255) / 256;
+        const double t_est = (double)rounds * cd.bm * cd.bn * cd.cost;
+        if (t_est < best_t * 0.999) {
+          best_t = t_est;
+          best = c;
+        }
+      }
+      switch (best) {
+        case 0: launch_pipe<256, 256, 2, 2, 2>(pa, st); break;
+        case 1: launch_pipe<256, 128, 4, 1, 3>(pa, st); break;
+        case 2: launch_pipe<128, 144, 4, 1, 4>(pa, st); break;
+        case 3: launch_pipe<128, 128, 2, 2, 4>(pa, st); break;
+        default: launch_pipe<64, 64, 2, 2, 4>(pa, st); break;
+      }
+      return hipGetLastError();
+    }
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((d + BN - 1) / BN);
     hipLaunchKernelGGL(k_gemm_bf16, dim3(tiles_m * tiles_n), dim3(256), 0, st, (int)M, (int)d,
