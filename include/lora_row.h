@@ -73,11 +73,11 @@ typedef enum lora_dtype {
 } lora_dtype_t;
 
 typedef enum lora_path {
-  LORA_PATH_AUTO = 0,    /* choose by row count per adapter */
-  LORA_PATH_GATHER = 1,  /* decode-sized: per-row gather, VALU dot products, wavefront
-                            reduction over k, A staged in LDS */
-  LORA_PATH_SGMV = 2     /* prefill-sized runs of rows sharing an adapter: MFMA tiles over
-                            the adapter-sorted segments */
+  LORA_PATH_AUTO = 0,    /* MFMA (SGMV) kernels where supported, else gather */
+  LORA_PATH_GATHER = 1,  /* VALU kernels: per-row gather, bf16 dot2 / fp32 FMA, wavefront
+                            reduction over k, A staged in LDS (any dtype, rank <= 256) */
+  LORA_PATH_SGMV = 2     /* MFMA tiles over the adapter-sorted segments (bf16, max_rank <= 64;
+                            LORA_ERR_UNSUPPORTED otherwise) */
 } lora_path_t;
 
 /* Flags for lora_linear. */
@@ -155,10 +155,14 @@ lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, con
  *   scales:      device fp32 [n_adapters]; scale of slot / adapter s.
  *   workspace:   device, >= lora_workspace_bytes(M, d, k, dtype, adapters).
  *   path:        lora_path_t; flags: LORA_FLAG_* (0 for none).
- * Steps, all on `stream`: plan (validate ids, stable sort of adapted rows
- * by adapter, segment and work-item tables), base GEMM y = x W^T, shrink
- * t = x A_s^T over k into fp32 partials, expand y += scale_s t B_s^T on
- * adapted rows only.  Rows with no adapter are written once, by the GEMM.
+ * Steps: plan (validate ids, stable sort of adapted rows by adapter,
+ * segment and work-item tables), base GEMM y = x W^T, shrink t = x A_s^T
+ * over k into fp32 partials (one per k split), expand y += scale_s t B_s^T
+ * on adapted rows only (t = the partials summed in split order).  All run
+ * on `stream` except the plan, which the library runs on its own side
+ * stream (one per device, default priority) beside the GEMM, joined by an
+ * event before the shrink; from the caller's view the call is ordered on
+ * `stream` as usual.  Rows with no adapter are written once, by the GEMM.
  * Results are run-to-run deterministic (no floating-point atomics).
  */
 lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
@@ -166,6 +170,40 @@ lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, c
                           const lora_adapters_t *adapters, const int32_t *adapter_ids,
                           const float *scales, void *y, int64_t ldy, void *workspace,
                           size_t workspace_bytes, int32_t path, uint32_t flags, void *stream);
+
+/*
+ * Several projections of the same input in one call -- e.g. the q and v
+ * projections of an attention layer ("Your LoRA Adapters Are Thrashing Your
+ * GPUs", section 02: Q and V are the usual adapted pair; section 01 shows
+ * each adapted projection as W + B A applied to the same x).  Slice i is a
+ * LoRA linear layer of width d_i with its own adapter set and scales; all
+ * slices share x, the per-row adapter_ids and one plan.
+ *   W: [sum_i d_i, k] -- the slices' base weights stacked by rows (slice 0
+ *      first), ldw >= k.
+ *   y: [M, sum_i d_i] -- slice i owns columns [sum_{j<i} d_j, + d_i).
+ *   slices: HOST array of n_slices (1..LORA_MAX_SLICES) descriptors; every
+ *      slice has the same n_adapters (an adapter that does not touch a
+ *      slice has rank 0 there).
+ * One GEMM over the stacked W, one shrink and one expand launch cover all
+ * slices (x is read once by the shrink).  A row is adapted only if its
+ * adapter is valid in every slice (else it is counted and gets the base).
+ * lora_linear is this call with one slice.
+ */
+#define LORA_MAX_SLICES 4
+typedef struct lora_slice {
+  int64_t d;                 /* output columns of this slice */
+  const float *scales;       /* device fp32 [n_adapters] */
+  lora_adapters_t adapters;  /* this slice's adapter set */
+} lora_slice_t;
+
+size_t lora_workspace_bytes_sliced(int64_t max_rows, int64_t k, lora_dtype_t dtype,
+                                   int32_t n_slices, const lora_slice_t *slices);
+
+lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
+                                 int64_t ldx, const void *W, int64_t ldw, int32_t n_slices,
+                                 const lora_slice_t *slices, const int32_t *adapter_ids, void *y,
+                                 int64_t ldy, void *workspace, size_t workspace_bytes,
+                                 int32_t path, uint32_t flags, void *stream);
 
 /*
  * The plan step alone (what lora_linear runs first): classify rows, sort

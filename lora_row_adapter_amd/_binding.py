@@ -48,6 +48,14 @@ class _CAdapters(ctypes.Structure):
     ]
 
 
+class _CSlice(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int64),
+        ("scales", ctypes.c_void_p),
+        ("adapters", _CAdapters),
+    ]
+
+
 class _CPlanView(ctypes.Structure):
     _fields_ = [
         ("counters", ctypes.c_void_p),
@@ -97,6 +105,12 @@ def load_library():
     lib.lora_linear.argtypes = [i32, i64, i64, i64, p, i64, p, i64, pad, p, p, p, i64, p, sz, i32,
                                 u32, p]
     lib.lora_linear.restype = i32
+    psl = ctypes.POINTER(_CSlice)
+    lib.lora_workspace_bytes_sliced.argtypes = [i64, i64, i32, i32, psl]
+    lib.lora_workspace_bytes_sliced.restype = sz
+    lib.lora_linear_sliced.argtypes = [i32, i64, i64, p, i64, p, i64, i32, psl, p, p, i64, p, sz,
+                                       i32, u32, p]
+    lib.lora_linear_sliced.restype = i32
     lib.lora_plan.argtypes = [i64, i64, i64, i32, pad, p, p, sz, p]
     lib.lora_plan.restype = i32
     lib.lora_plan_view.argtypes = [p, sz, i64, pad, ctypes.POINTER(_CPlanView)]
@@ -219,6 +233,38 @@ class Adapters:
         return ctypes.byref(self._c)
 
 
+class Slice:
+    """One projection of a multi-slice call: width d, its adapter set and
+    its per-adapter scales (device fp32 [n_adapters])."""
+
+    def __init__(self, d: int, adapters: Adapters, scales: torch.Tensor):
+        self.d = int(d)
+        self.adapters = adapters
+        self.scales = scales
+
+    def c(self) -> _CSlice:
+        c = _CSlice()
+        c.d = self.d
+        c.scales = _dev(self.scales, "scales", torch.float32)
+        c.adapters = self.adapters._c
+        return c
+
+
+def _slice_array(slices):
+    arr = (_CSlice * len(slices))()
+    for i, sl in enumerate(slices):
+        arr[i] = sl.c()
+    return arr
+
+
+def workspace_bytes_sliced(max_rows: int, k: int, dtype: torch.dtype, slices) -> int:
+    arr = _slice_array(slices)
+    n = load_library().lora_workspace_bytes_sliced(int(max_rows), int(k), _DTYPES[dtype], len(slices), arr)
+    if n == 0:
+        raise LoraError(1, "lora_workspace_bytes_sliced")
+    return int(n)
+
+
 def workspace_bytes(max_rows: int, d: int, k: int, dtype: torch.dtype, adapters: Adapters) -> int:
     n = load_library().lora_workspace_bytes(int(max_rows), int(d), int(k), _DTYPES[dtype], adapters.ref())
     if n == 0:
@@ -275,6 +321,39 @@ def lora_linear(x: torch.Tensor, W: torch.Tensor, adapters: Adapters, adapter_id
                          _dev(workspace, "workspace"), workspace.numel(), int(path), int(flags),
                          _stream_ptr(stream))
     _check(st, "lora_linear")
+    return y
+
+
+def lora_linear_sliced(x: torch.Tensor, W: torch.Tensor, slices, adapter_ids: torch.Tensor,
+                       y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       path: int = PATH_AUTO, flags: int = 0, stream=None) -> torch.Tensor:
+    """Several LoRA projections of the same x in one call.
+
+    W is the slices' base weights stacked by rows, [sum d_i, k]; y is
+    [M, sum d_i] with slice i in its own column range."""
+    lib = load_library()
+    M, k = x.shape
+    d_total = sum(sl.d for sl in slices)
+    if W.shape[0] != d_total:
+        raise ValueError("W must stack the slices' weights: %d rows expected" % d_total)
+    if y is None:
+        y = torch.empty((M, d_total), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes_sliced(M, k, x.dtype, slices), dtype=torch.uint8,
+                                device=x.device)
+    xp, ldx = _rows(x, "x")
+    wp, ldw = _rows(W, "W")
+    yp, ldy = _rows(y, "y")
+    if W.dtype != x.dtype or y.dtype != x.dtype:
+        raise TypeError("x, W, y must share a dtype")
+    if adapter_ids.numel() != M:
+        raise ValueError("adapter_ids must have one entry per row")
+    arr = _slice_array(slices)
+    st = lib.lora_linear_sliced(_dtype_code(x), M, k, xp, ldx, wp, ldw, len(slices), arr,
+                                _dev(adapter_ids, "adapter_ids", torch.int32), yp, ldy,
+                                _dev(workspace, "workspace"), workspace.numel(), int(path),
+                                int(flags), _stream_ptr(stream))
+    _check(st, "lora_linear_sliced")
     return y
 
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblora_row.so")
-SOURCES = ["lora_api.cpp", "plan.hip", "gemm.hip", "lora_gather.hip"]
+SOURCES = ["lora_api.cpp", "plan.hip", "gemm.hip", "lora_gather.hip", "lora_sgmv.hip"]
 ARCH = os.environ.get("LORA_ROW_ARCH", "gfx950")
 
 

@@ -16,6 +16,7 @@ constexpr int kRowsPerGatherItem = 16;  // rows per shrink/expand work item (gat
 constexpr int kRowsPerSgmvItem = 64;    // rows per work item (SGMV path)
 constexpr int kMaxKSplit = 16;          // k-splits of the shrink (fp32 partials)
 constexpr int kMaxRank = 256;
+constexpr int kMaxSlices = 4;           // projections sharing x in one call (e.g. q, k, v, o)
 
 // Header words at the start of a workspace (int32).
 enum HdrWord {
@@ -48,12 +49,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 
 // Work item of the LoRA kernels: `nrows` consecutive entries of the sorted
-// row permutation starting at `pos`, all using adapter `adapter` of rank `rank`.
+// row permutation starting at `pos`, all using adapter `adapter`.
 struct Item {
   int32_t adapter;
   int32_t pos;
   int32_t nrows;
-  int32_t rank;
+  int32_t seg;
 };
 
 // Where one adapter's A and B live.  SLOTS: A [S, R, k] and B [S, d, R];
@@ -94,6 +95,41 @@ __device__ __forceinline__ const uint8_t *adapter_b_ptr(const AdapterRef &ar, in
   int64_t off = ((int64_t)r * ar.k + n * r + j) * ar.elem_bytes;
   int64_t page = ar.page_table[(int64_t)s * ar.max_pages + (off >> ar.page_shift)];
   return ar.pool + (page << ar.page_shift) + (off & (ar.page_bytes - 1));
+}
+
+// One projection of a multi-slice call: its adapters, scales and the
+// columns [col0, col0 + d) of y it owns.
+struct SliceRef {
+  AdapterRef ar;
+  const int32_t *ranks;
+  const float *scales;
+  int64_t d;
+  int64_t col0;
+};
+
+// Index of the fp32 shrink partial of (sorted position p, slice s, rank j,
+// k split q).  The split index is innermost so a reader sums one contiguous
+// run of kMaxKSplit floats.
+__device__ __forceinline__ int64_t tpart_index(int64_t p, int s, int j, int q, int n_slices,
+                                               int R) {
+  return (((p * n_slices + s) * R + j) * kMaxKSplit) + q;
+}
+
+// Sum of the k-split partials of (p, s, j): one 64-byte run, read as four
+// 16-byte vectors; slots past `ksplit` (never written) are masked out.
+__device__ __forceinline__ float tpart_sum(const float *tpart, int64_t p, int s, int j, int ksplit,
+                                           int n_slices, int R) {
+  const float4 *q4 = reinterpret_cast<const float4 *>(tpart + tpart_index(p, s, j, 0, n_slices, R));
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxKSplit / 4; ++i) {
+    const float4 f = q4[i];
+    v += (4 * i + 0 < ksplit) ? f.x : 0.f;
+    v += (4 * i + 1 < ksplit) ? f.y : 0.f;
+    v += (4 * i + 2 < ksplit) ? f.z : 0.f;
+    v += (4 * i + 3 < ksplit) ? f.w : 0.f;
+  }
+  return v;
 }
 
 }  // namespace lora

@@ -19,21 +19,27 @@ struct WsLayout {
   size_t hdr = 0, perm = 0, seg_adapter = 0, seg_start = 0, seg_len = 0;
   size_t items_g = 0, items_s = 0, tpart = 0, total = 0;
 };
-WsLayout ws_layout(int64_t rows, int32_t S, int32_t R);
+WsLayout ws_layout(int64_t rows, int32_t S, int32_t R, int32_t n_slices);
 
-struct PlanArgs {
-  const int32_t *ids;
+// Per-slice validity data the plan checks for each adapter.
+struct PlanSlice {
   const int32_t *ranks;
-  int32_t M;
-  int32_t S;
   int32_t R;
-  int32_t row_bits;  // log2 of the sort width
   // pool checks (page_table == nullptr for slots)
   const int32_t *page_table;
   int32_t max_pages;
   int64_t n_pages;
   int64_t page_bytes;
   int64_t bytes_per_rank;  // (k + d) * elem_bytes
+};
+
+struct PlanArgs {
+  const int32_t *ids;
+  int32_t M;
+  int32_t S;
+  int32_t row_bits;  // log2 of the sort width
+  int32_t n_slices;
+  PlanSlice sl[kMaxSlices];
   // outputs
   uint8_t *ws;
   WsLayout L;
@@ -41,13 +47,15 @@ struct PlanArgs {
 
 struct LoraArgs {
   int32_t dtype;  // 0 f32, 1 bf16
-  int64_t k, d;
+  int64_t k;
   const void *x;
   int64_t ldx;
   void *y;
   int64_t ldy;
-  const float *scales;
-  AdapterRef ar;
+  int32_t n_slices;
+  int32_t R;        // max rank over slices (partials row width)
+  SliceRef sl[kMaxSlices];
+  int32_t col_blk[kMaxSlices + 1];  // prefix of expand column blocks per slice
   uint8_t *ws;
   WsLayout L;
   int32_t ksplit;
@@ -62,7 +70,8 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
                        const void *W, int64_t ldw, void *y, int64_t ldy, hipStream_t st);
 hipError_t launch_shrink_gather(const LoraArgs &a, hipStream_t st);
 hipError_t launch_expand_gather(const LoraArgs &a, hipStream_t st);
-hipError_t launch_shrink_sgmv(const LoraArgs &a, hipStream_t st);
-hipError_t launch_expand_sgmv(const LoraArgs &a, hipStream_t st);
+hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, hipStream_t st);
+hipError_t launch_expand_sgmv(const LoraArgs &a, int rows_per_item, hipStream_t st);
+constexpr int kMaxRankMfma = 64;
 
 }  // namespace lora

@@ -16,7 +16,7 @@ namespace lora {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(int64_t rows, int32_t S, int32_t R) {
+WsLayout ws_layout(int64_t rows, int32_t S, int32_t R, int32_t n_slices) {
   WsLayout L;
   L.rows = std::max<int64_t>(1, rows);
   L.R = R;
@@ -36,7 +36,7 @@ WsLayout ws_layout(int64_t rows, int32_t S, int32_t R) {
   L.seg_len = take((size_t)L.seg_cap * sizeof(int32_t));
   L.items_g = take((size_t)L.items_g_cap * sizeof(Item));
   L.items_s = take((size_t)L.items_s_cap * sizeof(Item));
-  L.tpart = take((size_t)kMaxKSplit * L.rows * R * sizeof(float));
+  L.tpart = take((size_t)kMaxKSplit * L.rows * n_slices * R * sizeof(float));
   L.total = off;
   return L;
 }
@@ -85,6 +85,45 @@ void end(int i, hipStream_t st) {
   (void)hipEventRecord(ev1[i], st);
 }
 }  // namespace prof
+
+// ---------------------------------------------------------------------------
+// Side stream for the plan: the plan depends only on the ids, the GEMM only
+// on x and W, so the plan runs beside the GEMM and the caller's stream waits
+// for it before the shrink.  One non-blocking stream (default priority) and
+// a ring of events per device, created on first use and kept.
+// ---------------------------------------------------------------------------
+namespace side {
+constexpr int kMaxDev = 64;
+constexpr int kEvents = 16;
+std::mutex mu;
+struct Dev {
+  bool tried = false, ok = false;
+  hipStream_t s = nullptr;
+  hipEvent_t ev[kEvents];
+  int next = 0;
+};
+Dev devs[kMaxDev];
+
+bool get(hipStream_t *s, hipEvent_t *fork, hipEvent_t *join) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDev) return false;
+  std::lock_guard<std::mutex> g(mu);
+  Dev &D = devs[d];
+  if (!D.tried) {
+    D.tried = true;
+    if (hipStreamCreateWithFlags(&D.s, hipStreamNonBlocking) != hipSuccess) return false;
+    for (int i = 0; i < kEvents; ++i)
+      if (hipEventCreateWithFlags(&D.ev[i], hipEventDisableTiming) != hipSuccess) return false;
+    D.ok = true;
+  }
+  if (!D.ok) return false;
+  *s = D.s;
+  *fork = D.ev[D.next];
+  *join = D.ev[D.next + 1];
+  D.next = (D.next + 2) % kEvents;
+  return true;
+}
+}  // namespace side
 
 template <typename F>
 static hipError_t timed(int c, hipStream_t st, F &&launch) {
@@ -182,13 +221,46 @@ const char *lora_status_str(lora_status_t s) {
   return "unknown status";
 }
 
+// Validate a slice list; fills S (common adapter count) and R (max rank).
+static lora_status_t check_slices(int32_t n_slices, const lora_slice_t *slices, int64_t rows_cap,
+                                  int32_t *S_out, int32_t *R_out, int64_t *d_total) {
+  if (slices == nullptr || n_slices < 1 || n_slices > LORA_MAX_SLICES) return LORA_ERR_ARG;
+  int32_t R = 0;
+  int64_t dt = 0;
+  for (int q = 0; q < n_slices; ++q) {
+    const lora_status_t s = check_adapters(&slices[q].adapters, rows_cap);
+    if (s != LORA_OK) return s;
+    if (slices[q].adapters.n_adapters != slices[0].adapters.n_adapters) return LORA_ERR_ARG;
+    if (slices[q].d < 1 || slices[q].d > INT32_MAX) return LORA_ERR_SHAPE;
+    R = std::max(R, slices[q].adapters.max_rank);
+    dt += slices[q].d;
+  }
+  if (dt > INT32_MAX) return LORA_ERR_SHAPE;
+  *S_out = slices[0].adapters.n_adapters;
+  *R_out = R;
+  *d_total = dt;
+  return LORA_OK;
+}
+
+size_t lora_workspace_bytes_sliced(int64_t max_rows, int64_t k, lora_dtype_t dtype,
+                                   int32_t n_slices, const lora_slice_t *slices) {
+  if (max_rows < 0 || k < 1) return 0;
+  if (dtype != LORA_DTYPE_F32 && dtype != LORA_DTYPE_BF16) return 0;
+  int32_t S = 0, R = 0;
+  int64_t dt = 0;
+  if (check_slices(n_slices, slices, max_rows, &S, &R, &dt) != LORA_OK) return 0;
+  const int64_t rows = std::min<int64_t>(std::max<int64_t>(max_rows, 1), kPlanMaxRows);
+  return ws_layout(rows, S, R, n_slices).total;
+}
+
 size_t lora_workspace_bytes(int64_t max_rows, int64_t d, int64_t k, lora_dtype_t dtype,
                             const lora_adapters_t *adapters) {
-  if (max_rows < 0 || d < 1 || k < 1) return 0;
-  if (dtype != LORA_DTYPE_F32 && dtype != LORA_DTYPE_BF16) return 0;
-  if (check_adapters(adapters, max_rows) != LORA_OK) return 0;
-  const int64_t rows = std::min<int64_t>(std::max<int64_t>(max_rows, 1), kPlanMaxRows);
-  return ws_layout(rows, adapters->n_adapters, adapters->max_rank).total;
+  if (adapters == nullptr) return 0;
+  lora_slice_t s{};
+  s.d = d;
+  s.scales = nullptr;
+  s.adapters = *adapters;
+  return lora_workspace_bytes_sliced(max_rows, k, dtype, 1, &s);
 }
 
 lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
@@ -203,22 +275,28 @@ lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, con
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
-static lora_status_t run_plan(int64_t M, int64_t k, int64_t d, lora_dtype_t dtype,
-                              const lora_adapters_t *ad, const int32_t *ids, uint8_t *ws,
+static lora_status_t run_plan(int64_t M, int64_t k, lora_dtype_t dtype, int32_t n_slices,
+                              const lora_slice_t *slices, const int32_t *ids, uint8_t *ws,
                               const WsLayout &L, hipStream_t st) {
   PlanArgs p{};
   p.ids = ids;
-  p.ranks = ad->ranks;
   p.M = (int32_t)M;
-  p.S = ad->n_adapters;
-  p.R = ad->max_rank;
+  p.S = slices[0].adapters.n_adapters;
   p.row_bits = row_bits_for(std::max<int64_t>(M, 2));
-  if (ad->kind == LORA_ADAPTERS_POOL) {
-    p.page_table = ad->page_table;
-    p.max_pages = ad->max_pages;
-    p.n_pages = ad->n_pages;
-    p.page_bytes = ad->page_bytes;
-    p.bytes_per_rank = (k + d) * (dtype == LORA_DTYPE_BF16 ? 2 : 4);
+  p.n_slices = n_slices;
+  const int64_t eb = dtype == LORA_DTYPE_BF16 ? 2 : 4;
+  for (int q = 0; q < n_slices; ++q) {
+    const lora_adapters_t &ad = slices[q].adapters;
+    PlanSlice &ps = p.sl[q];
+    ps.ranks = ad.ranks;
+    ps.R = ad.max_rank;
+    if (ad.kind == LORA_ADAPTERS_POOL) {
+      ps.page_table = ad.page_table;
+      ps.max_pages = ad.max_pages;
+      ps.n_pages = ad.n_pages;
+      ps.page_bytes = ad.page_bytes;
+      ps.bytes_per_rank = (k + slices[q].d) * eb;
+    }
   }
   p.ws = ws;
   p.L = L;
@@ -226,19 +304,33 @@ static lora_status_t run_plan(int64_t M, int64_t k, int64_t d, lora_dtype_t dtyp
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
-lora_status_t lora_plan(int64_t M, int64_t k, int64_t d, lora_dtype_t dtype,
-                        const lora_adapters_t *adapters, const int32_t *adapter_ids,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+static lora_status_t plan_common(int64_t M, int64_t k, lora_dtype_t dtype, int32_t n_slices,
+                                 const lora_slice_t *slices, const int32_t *adapter_ids,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
   if (dtype != LORA_DTYPE_F32 && dtype != LORA_DTYPE_BF16) return LORA_ERR_DTYPE;
-  if (M < 0 || M > kPlanMaxRows || k < 1 || d < 1) return LORA_ERR_SHAPE;
-  lora_status_t s = check_adapters(adapters, M);
+  if (M < 0 || M > kPlanMaxRows || k < 1) return LORA_ERR_SHAPE;
+  int32_t S = 0, R = 0;
+  int64_t dt = 0;
+  lora_status_t s = check_slices(n_slices, slices, M, &S, &R, &dt);
   if (s != LORA_OK) return s;
   if (workspace == nullptr || (M > 0 && adapter_ids == nullptr)) return LORA_ERR_ARG;
   if (((uintptr_t)workspace & 255u) != 0) return LORA_ERR_WORKSPACE;
-  const WsLayout L = ws_layout(std::max<int64_t>(M, 1), adapters->n_adapters, adapters->max_rank);
+  const WsLayout L = ws_layout(std::max<int64_t>(M, 1), S, R, n_slices);
   if (workspace_bytes < L.total) return LORA_ERR_WORKSPACE;
   // M == 0 runs too: the kernel then writes an empty plan (zero counts).
-  return run_plan(M, k, d, dtype, adapters, adapter_ids, (uint8_t *)workspace, L, (hipStream_t)stream);
+  return run_plan(M, k, dtype, n_slices, slices, adapter_ids, (uint8_t *)workspace, L,
+                  (hipStream_t)stream);
+}
+
+lora_status_t lora_plan(int64_t M, int64_t k, int64_t d, lora_dtype_t dtype,
+                        const lora_adapters_t *adapters, const int32_t *adapter_ids,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (adapters == nullptr) return LORA_ERR_ARG;
+  lora_slice_t sl{};
+  sl.d = d;
+  sl.adapters = *adapters;
+  if (d < 1) return LORA_ERR_SHAPE;
+  return plan_common(M, k, dtype, 1, &sl, adapter_ids, workspace, workspace_bytes, stream);
 }
 
 lora_status_t lora_plan_view(const void *workspace, size_t workspace_bytes, int64_t M,
@@ -247,7 +339,7 @@ lora_status_t lora_plan_view(const void *workspace, size_t workspace_bytes, int6
   if (M < 0 || M > kPlanMaxRows) return LORA_ERR_SHAPE;
   lora_status_t s = check_adapters(adapters, M);
   if (s != LORA_OK) return s;
-  const WsLayout L = ws_layout(std::max<int64_t>(M, 1), adapters->n_adapters, adapters->max_rank);
+  const WsLayout L = ws_layout(std::max<int64_t>(M, 1), adapters->n_adapters, adapters->max_rank, 1);
   if (workspace_bytes < L.total) return LORA_ERR_WORKSPACE;
   const uint8_t *w = (const uint8_t *)workspace;
   out->counters = (const int32_t *)(w + L.hdr);
@@ -259,72 +351,142 @@ lora_status_t lora_plan_view(const void *workspace, size_t workspace_bytes, int6
   return LORA_OK;
 }
 
-lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
-                          int64_t ldx, const void *W, int64_t ldw,
-                          const lora_adapters_t *adapters, const int32_t *adapter_ids,
-                          const float *scales, void *y, int64_t ldy, void *workspace,
-                          size_t workspace_bytes, int32_t path, uint32_t flags, void *stream) {
-  lora_status_t s = check_gemm_args(dtype, M, k, d, x, ldx, W, ldw, y, ldy);
+lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
+                                 int64_t ldx, const void *W, int64_t ldw, int32_t n_slices,
+                                 const lora_slice_t *slices, const int32_t *adapter_ids, void *y,
+                                 int64_t ldy, void *workspace, size_t workspace_bytes,
+                                 int32_t path, uint32_t flags, void *stream) {
+  int32_t S = 0, R = 0;
+  int64_t d_total = 0;
+  if (slices == nullptr || n_slices < 1 || n_slices > LORA_MAX_SLICES) return LORA_ERR_ARG;
+  lora_status_t s = check_slices(n_slices, slices, M, &S, &R, &d_total);
+  if (s != LORA_OK) return s;
+  s = check_gemm_args(dtype, M, k, d_total, x, ldx, W, ldw, y, ldy);
   if (s != LORA_OK) return s;
   if (path != LORA_PATH_AUTO && path != LORA_PATH_GATHER && path != LORA_PATH_SGMV) return LORA_ERR_ARG;
   if ((flags & ~LORA_FLAG_REUSE_PLAN) != 0) return LORA_ERR_ARG;
-  s = check_adapters(adapters, M);
-  if (s != LORA_OK) return s;
   if (M == 0) return LORA_OK;
-  if (adapter_ids == nullptr || scales == nullptr || workspace == nullptr) return LORA_ERR_ARG;
+  if (adapter_ids == nullptr || workspace == nullptr) return LORA_ERR_ARG;
+  for (int q = 0; q < n_slices; ++q)
+    if (slices[q].scales == nullptr) return LORA_ERR_ARG;
   if (((uintptr_t)workspace & 255u) != 0) return LORA_ERR_WORKSPACE;
   if ((flags & LORA_FLAG_REUSE_PLAN) && M > kPlanMaxRows) return LORA_ERR_ARG;
   const int64_t first = std::min<int64_t>(M, kPlanMaxRows);
-  if (workspace_bytes < ws_layout(first, adapters->n_adapters, adapters->max_rank).total)
-    return LORA_ERR_WORKSPACE;
-  if (path == LORA_PATH_SGMV) return LORA_ERR_UNSUPPORTED;
+  if (workspace_bytes < ws_layout(first, S, R, n_slices).total) return LORA_ERR_WORKSPACE;
+
+  // kernel family: MFMA tiles need bf16 operands and ranks <= 64
+  const bool mfma_ok = dtype == LORA_DTYPE_BF16 && R <= kMaxRankMfma;
+  bool use_mfma;
+  if (path == LORA_PATH_SGMV) {
+    if (!mfma_ok) return LORA_ERR_UNSUPPORTED;
+    use_mfma = true;
+  } else if (path == LORA_PATH_GATHER) {
+    use_mfma = false;
+  } else {
+    use_mfma = mfma_ok;
+  }
 
   hipStream_t st = (hipStream_t)stream;
   const int32_t eb = dtype == LORA_DTYPE_BF16 ? 2 : 4;
-  const AdapterRef ar = make_ref(adapters, k, d, eb);
   uint8_t *ws = (uint8_t *)workspace;
+
+  LoraArgs a{};
+  a.dtype = dtype;
+  a.k = k;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.n_slices = n_slices;
+  a.R = R;
+  a.ws = ws;
+  int64_t col0 = 0;
+  for (int q = 0; q < n_slices; ++q) {
+    SliceRef &sr = a.sl[q];
+    sr.ar = make_ref(&slices[q].adapters, k, slices[q].d, eb);
+    sr.ranks = slices[q].adapters.ranks;
+    sr.scales = slices[q].scales;
+    sr.d = slices[q].d;
+    sr.col0 = col0;
+    col0 += slices[q].d;
+  }
 
   for (int64_t c0 = 0; c0 < M; c0 += kPlanMaxRows) {
     const int64_t Mc = std::min<int64_t>(kPlanMaxRows, M - c0);
-    const WsLayout L = ws_layout(Mc, adapters->n_adapters, adapters->max_rank);
+    const WsLayout L = ws_layout(Mc, S, R, n_slices);
     const uint8_t *xc = (const uint8_t *)x + c0 * ldx * eb;
     uint8_t *yc = (uint8_t *)y + c0 * ldy * eb;
+    hipStream_t ps = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    const bool fork = !(flags & LORA_FLAG_REUSE_PLAN) && side::get(&ps, &ev_fork, &ev_join);
     if (!(flags & LORA_FLAG_REUSE_PLAN)) {
-      s = run_plan(Mc, k, d, dtype, adapters, adapter_ids + c0, ws, L, st);
+      if (fork) {
+        if (hipEventRecord(ev_fork, st) != hipSuccess || hipStreamWaitEvent(ps, ev_fork, 0) != hipSuccess)
+          return LORA_ERR_HIP;
+      }
+      s = run_plan(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L, fork ? ps : st);
       if (s != LORA_OK) return s;
+      if (fork && hipEventRecord(ev_join, ps) != hipSuccess) return LORA_ERR_HIP;
     }
     hipError_t e = timed(LORA_K_GEMM, st, [&] {
-      return launch_gemm(dtype, Mc, k, d, xc, ldx, W, ldw, yc, ldy, st);
+      return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, st);
     });
     if (e != hipSuccess) return LORA_ERR_HIP;
+    if (fork && hipStreamWaitEvent(st, ev_join, 0) != hipSuccess) return LORA_ERR_HIP;
 
-    LoraArgs a{};
-    a.dtype = dtype;
-    a.k = k;
-    a.d = d;
     a.x = xc;
-    a.ldx = ldx;
     a.y = yc;
-    a.ldy = ldy;
-    a.scales = scales;
-    a.ar = ar;
-    a.ws = ws;
     a.L = L;
-    // k splits: aim for ~1024 shrink workgroups on the 256 CUs.
-    const int64_t est_items = (Mc + kRowsPerGatherItem - 1) / kRowsPerGatherItem +
-                              std::min<int64_t>({(int64_t)adapters->n_adapters, Mc, 64});
-    int64_t ks = std::max<int64_t>(1, std::min<int64_t>(kMaxKSplit, (1024 + est_items - 1) / est_items));
+    // rows per MFMA work item: 64-row segment tiles when asked for (SGMV)
+    // or when adapters are expected to hold long runs of rows (prefill);
+    // else 16, which gives decode batches more workgroups
+    const int64_t segs = std::min<int64_t>((int64_t)S, Mc);
+    const int rpi = (use_mfma && (path == LORA_PATH_SGMV ||
+                            Mc / std::max<int64_t>(segs, 1) >= 128))
+                  ? kRowsPerSgmvItem
+                  : kRowsPerGatherItem;
+
+    // k splits: aim for ~600 shrink workgroups on the 256 CUs (measured
+    // best for decode batches: more splits add partials for the expand to
+    // sum, fewer leave CUs idle)
+    const int64_t est_items = (Mc + rpi - 1) / rpi + std::min<int64_t>(segs, 64);
+    const int64_t jblk = use_mfma ? 1 : (R + 15) / 16;
+    const int64_t per_split =
+        std::max<int64_t>(1, est_items * n_slices * (use_mfma ? 1 : std::min<int64_t>(jblk, 2)));
+    int64_t ks = std::max<int64_t>(1, std::min<int64_t>(kMaxKSplit, (600 + per_split - 1) / per_split));
     int64_t kchunk = (k + ks - 1) / ks;
     kchunk = (kchunk + 255) / 256 * 256;
     ks = (k + kchunk - 1) / kchunk;
     a.ksplit = (int32_t)ks;
     a.kchunk = kchunk;
-    e = timed(LORA_K_SHRINK, st, [&] { return launch_shrink_gather(a, st); });
-    if (e != hipSuccess) return LORA_ERR_HIP;
-    e = timed(LORA_K_EXPAND, st, [&] { return launch_expand_gather(a, st); });
-    if (e != hipSuccess) return LORA_ERR_HIP;
+    if (use_mfma) {
+      e = timed(LORA_K_SGMV_SHRINK, st, [&] { return launch_shrink_sgmv(a, rpi, st); });
+      if (e != hipSuccess) return LORA_ERR_HIP;
+      e = timed(LORA_K_SGMV_EXPAND, st, [&] { return launch_expand_sgmv(a, rpi, st); });
+      if (e != hipSuccess) return LORA_ERR_HIP;
+    } else {
+      e = timed(LORA_K_SHRINK, st, [&] { return launch_shrink_gather(a, st); });
+      if (e != hipSuccess) return LORA_ERR_HIP;
+      e = timed(LORA_K_EXPAND, st, [&] { return launch_expand_gather(a, st); });
+      if (e != hipSuccess) return LORA_ERR_HIP;
+    }
   }
   return LORA_OK;
+}
+
+lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
+                          int64_t ldx, const void *W, int64_t ldw,
+                          const lora_adapters_t *adapters, const int32_t *adapter_ids,
+                          const float *scales, void *y, int64_t ldy, void *workspace,
+                          size_t workspace_bytes, int32_t path, uint32_t flags, void *stream) {
+  if (adapters == nullptr) return LORA_ERR_ARG;
+  if (dtype != LORA_DTYPE_F32 && dtype != LORA_DTYPE_BF16) return LORA_ERR_DTYPE;
+  if (d < 1) return LORA_ERR_SHAPE;
+  lora_slice_t sl{};
+  sl.d = d;
+  sl.scales = scales;
+  sl.adapters = *adapters;
+  if (M > 0 && scales == nullptr) return LORA_ERR_ARG;
+  return lora_linear_sliced(dtype, M, k, x, ldx, W, ldw, 1, &sl, adapter_ids, y, ldy, workspace,
+                            workspace_bytes, path, flags, stream);
 }
 
 lora_status_t lora_translate(const lora_adapters_t *adapters, const int32_t *adapter,

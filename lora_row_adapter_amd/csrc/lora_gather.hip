@@ -11,7 +11,7 @@
 // permutation that share one adapter.
 //
 // shrink: t[p, j] = sum_k A_s[j, k] x[perm[p], k]   (j < r_s, k -> r)
-//   grid (item, 16-rank block, k split).  A_s[j0:j0+16, kc:kc+256] is staged
+//   grid (item, slice x 16-rank block, k split).  A_s[j0:j0+16, kc:kc+256] is staged
 //   in LDS once per 256-wide k step and reused by the 16 rows of the item
 //   (4 rows per wave).  Each lane owns 4 consecutive k and keeps 4 x 16
 //   partial sums (bf16 pairs through v_dot2_f32_bf16, fp32 through FMA); the
@@ -19,8 +19,9 @@
 //   output (row = lane / 16, rank = lane % 16) in lane `lane`.  Each k split
 //   writes its own fp32 partial; no atomics.
 // expand: y[perm[p], n] += scale_s * sum_j B_s[n, j] t[p, j]   (r -> d)
-//   grid (item, 512-column block).  The k-split partials are summed in
-//   ascending split order into LDS, then each thread owns two columns and
+//   grid (item, 512-column block of any slice).  The k-split partials of the
+//   item's rows are summed in split order into LDS, then each thread owns
+//   two columns and
 //   all rows of the item: acc = sum_j B t in fp32, then y = y + scale * acc
 //   rounded once.  Rows without an adapter are never touched.
 #include "kernels.hpp"
@@ -82,8 +83,11 @@ __global__ __launch_bounds__(256) void k_shrink_gather(LoraArgs a) {
   const int item = blockIdx.x;
   if (item >= hdr[kHdrItemsGather]) return;
   const Item it = reinterpret_cast<const Item *>(a.ws + a.L.items_g)[item];
-  const int r = it.rank;
-  const int j0 = blockIdx.y * JB;
+  const int jblocks = (a.R + JB - 1) / JB;
+  const int slice = blockIdx.y / jblocks;
+  const SliceRef &sl = a.sl[slice];
+  const int r = sl.ranks[it.adapter];
+  const int j0 = (blockIdx.y - slice * jblocks) * JB;
   if (j0 >= r) return;
   const int nj = min(JB, r - j0);
   const int64_t kbeg = (int64_t)blockIdx.z * a.kchunk;
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256) void k_shrink_gather(LoraArgs a) {
       const int64_t kk = kc + (int64_t)c * (16 / EB);
       uint4 val = make_uint4(0, 0, 0, 0);
       if (jj < nj && kk < kend)
-        val = *reinterpret_cast<const uint4 *>(adapter_a_ptr(a.ar, it.adapter, r, j0 + jj, kk));
+        val = *reinterpret_cast<const uint4 *>(adapter_a_ptr(sl.ar, it.adapter, r, j0 + jj, kk));
       *reinterpret_cast<uint4 *>(&As[jj * ROWB + c * 16]) = val;
     }
     __syncthreads();
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(256) void k_shrink_gather(LoraArgs a) {
   const int jj = lane & 15;
   if (rowv[rr] && jj < nj) {
     const int64_t p = it.pos + wave * RPW + rr;
-    tpart[((int64_t)blockIdx.z * a.L.rows + p) * a.L.R + j0 + jj] = sum;
+    tpart[tpart_index(p, slice, j0 + jj, blockIdx.z, a.n_slices, a.R)] = sum;
   }
 }
 
@@ -191,7 +195,10 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
   const int item = blockIdx.x;
   if (item >= hdr[kHdrItemsGather]) return;
   const Item it = reinterpret_cast<const Item *>(a.ws + a.L.items_g)[item];
-  const int r = it.rank;
+  int slice = 0;
+  while (slice + 1 < a.n_slices && (int)blockIdx.y >= a.col_blk[slice + 1]) ++slice;
+  const SliceRef &sl = a.sl[slice];
+  const int r = sl.ranks[it.adapter];
   if (r == 0) return;
   const int nr = it.nrows;
   const int32_t *perm = reinterpret_cast<const int32_t *>(a.ws + a.L.perm);
@@ -201,29 +208,28 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
   for (int idx = tid; idx < nr * r; idx += 256) {
     const int row = idx / r;
     const int j = idx - row * r;
-    float s = 0.f;
-    for (int q = 0; q < a.ksplit; ++q) s += tpart[((int64_t)q * a.L.rows + it.pos + row) * a.L.R + j];
-    ts[row * kMaxRank + j] = s;
+    ts[row * kMaxRank + j] = tpart_sum(tpart, it.pos + row, slice, j, a.ksplit, a.n_slices, a.R);
   }
   __syncthreads();
 
-  const int64_t n = (int64_t)blockIdx.y * ECOLS + 2 * tid;
-  if (n >= a.d) return;
-  const bool c1 = n + 1 < a.d;
+  const int64_t n = (int64_t)(blockIdx.y - a.col_blk[slice]) * ECOLS + 2 * tid;
+  if (n >= sl.d) return;
+  const bool c1 = n + 1 < sl.d;
   float acc[kRowsPerGatherItem][2];
 #pragma unroll
   for (int i = 0; i < kRowsPerGatherItem; ++i) acc[i][0] = acc[i][1] = 0.f;
 
   // 16-byte vector loads of B rows where the row start is 16-byte aligned.
-  const bool vec_ok = a.ar.pooled ? ((r * EB) % 16 == 0) : ((a.ar.max_rank * EB) % 16 == 0);
+  const AdapterRef &ar = sl.ar;
+  const bool vec_ok = ar.pooled ? ((r * EB) % 16 == 0) : ((ar.max_rank * EB) % 16 == 0);
   const int jv = vec_ok ? (r / VEC) * VEC : 0;
-  const T *b0p = reinterpret_cast<const T *>(adapter_b_ptr(a.ar, it.adapter, r, n, 0));
-  const T *b1p = c1 ? reinterpret_cast<const T *>(adapter_b_ptr(a.ar, it.adapter, r, n + 1, 0)) : b0p;
+  const T *b0p = reinterpret_cast<const T *>(adapter_b_ptr(ar, it.adapter, r, n, 0));
+  const T *b1p = c1 ? reinterpret_cast<const T *>(adapter_b_ptr(ar, it.adapter, r, n + 1, 0)) : b0p;
   for (int j = 0; j < jv; j += VEC) {
     // a pooled row may continue on another page: translate each vector
-    const T *p0 = a.ar.pooled ? reinterpret_cast<const T *>(adapter_b_ptr(a.ar, it.adapter, r, n, j)) : b0p + j;
-    const T *p1 = a.ar.pooled ? reinterpret_cast<const T *>(adapter_b_ptr(a.ar, it.adapter, r, c1 ? n + 1 : n, j))
-                              : b1p + j;
+    const T *p0 = ar.pooled ? reinterpret_cast<const T *>(adapter_b_ptr(ar, it.adapter, r, n, j)) : b0p + j;
+    const T *p1 = ar.pooled ? reinterpret_cast<const T *>(adapter_b_ptr(ar, it.adapter, r, c1 ? n + 1 : n, j))
+                            : b1p + j;
     const uint4 u0 = *reinterpret_cast<const uint4 *>(p0);
     const uint4 u1 = c1 ? *reinterpret_cast<const uint4 *>(p1) : make_uint4(0, 0, 0, 0);
     float bv0[VEC], bv1[VEC];
@@ -256,8 +262,8 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
     }
   }
   for (int j = jv; j < r; ++j) {
-    const float bv0 = load_f32(reinterpret_cast<const T *>(adapter_b_ptr(a.ar, it.adapter, r, n, j)));
-    const float bv1 = c1 ? load_f32(reinterpret_cast<const T *>(adapter_b_ptr(a.ar, it.adapter, r, n + 1, j))) : 0.f;
+    const float bv0 = load_f32(reinterpret_cast<const T *>(adapter_b_ptr(ar, it.adapter, r, n, j)));
+    const float bv1 = c1 ? load_f32(reinterpret_cast<const T *>(adapter_b_ptr(ar, it.adapter, r, n + 1, j))) : 0.f;
 #pragma unroll
     for (int row = 0; row < kRowsPerGatherItem; ++row) {
       if (row < nr) {
@@ -268,19 +274,28 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
     }
   }
 
-  const float scale = a.scales[it.adapter];
-  T *yb = reinterpret_cast<T *>(a.y);
+  // y += scale * acc: all of this thread's y values are loaded before any
+  // is stored (a store could alias a later load, which would otherwise
+  // serialise every read-modify-write on the load latency)
+  const float scale = sl.scales[it.adapter];
+  T *yb = reinterpret_cast<T *>(a.y) + sl.col0;
+  T *yr[kRowsPerGatherItem];
+  T y0[kRowsPerGatherItem], y1[kRowsPerGatherItem];
 #pragma unroll
   for (int row = 0; row < kRowsPerGatherItem; ++row) {
-    if (row < nr) {
-      T *py = yb + (int64_t)perm[it.pos + row] * a.ldy + n;
-      if constexpr (DT == 1) {
-        py[0] = f32_to_bf16_bits(bf16_bits_to_f32(py[0]) + scale * acc[row][0]);
-        if (c1) py[1] = f32_to_bf16_bits(bf16_bits_to_f32(py[1]) + scale * acc[row][1]);
-      } else {
-        py[0] = py[0] + scale * acc[row][0];
-        if (c1) py[1] = py[1] + scale * acc[row][1];
-      }
+    yr[row] = row < nr ? yb + (int64_t)perm[it.pos + row] * a.ldy + n : nullptr;
+    y0[row] = yr[row] ? yr[row][0] : T(0);
+    y1[row] = (yr[row] && c1) ? yr[row][1] : T(0);
+  }
+#pragma unroll
+  for (int row = 0; row < kRowsPerGatherItem; ++row) {
+    if (yr[row] == nullptr) continue;
+    if constexpr (DT == 1) {
+      yr[row][0] = f32_to_bf16_bits(bf16_bits_to_f32(y0[row]) + scale * acc[row][0]);
+      if (c1) yr[row][1] = f32_to_bf16_bits(bf16_bits_to_f32(y1[row]) + scale * acc[row][1]);
+    } else {
+      yr[row][0] = y0[row] + scale * acc[row][0];
+      if (c1) yr[row][1] = y1[row] + scale * acc[row][1];
     }
   }
 }
@@ -288,7 +303,8 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
 }  // namespace
 
 hipError_t launch_shrink_gather(const LoraArgs &a, hipStream_t st) {
-  dim3 grid((unsigned)a.L.items_g_cap, (unsigned)((a.L.R + JB - 1) / JB), (unsigned)a.ksplit);
+  dim3 grid((unsigned)a.L.items_g_cap, (unsigned)(a.n_slices * ((a.R + JB - 1) / JB)),
+            (unsigned)a.ksplit);
   if (a.dtype == 1)
     hipLaunchKernelGGL(k_shrink_gather<1>, grid, dim3(256), 0, st, a);
   else
@@ -296,16 +312,17 @@ hipError_t launch_shrink_gather(const LoraArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_expand_gather(const LoraArgs &a, hipStream_t st) {
-  dim3 grid((unsigned)a.L.items_g_cap, (unsigned)((a.d + ECOLS - 1) / ECOLS));
+hipError_t launch_expand_gather(const LoraArgs &a0, hipStream_t st) {
+  LoraArgs a = a0;
+  a.col_blk[0] = 0;
+  for (int q = 0; q < a.n_slices; ++q)
+    a.col_blk[q + 1] = a.col_blk[q] + (int32_t)((a.sl[q].d + ECOLS - 1) / ECOLS);
+  dim3 grid((unsigned)a.L.items_g_cap, (unsigned)a.col_blk[a.n_slices]);
   if (a.dtype == 1)
     hipLaunchKernelGGL(k_expand_gather<1>, grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(k_expand_gather<0>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
-
-hipError_t launch_shrink_sgmv(const LoraArgs &, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_expand_sgmv(const LoraArgs &, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace lora

@@ -7,7 +7,8 @@
 // what the paper actually says ...", section "Batched LoRA computation": the
 // corrections run as one segmented operation over the adapter-sorted rows).
 //
-// One workgroup of 1024 threads does the whole plan for up to 8192 rows:
+// One workgroup (256 threads up to 1024 rows, else 1024) does the whole plan
+// for up to 8192 rows:
 //   1. classify each row (none / adapted / bad id / bad rank / bad page) and
 //      form the key (adapter << row_bits) | row, or a sentinel for rows that
 //      take no adapter;
@@ -24,9 +25,10 @@ namespace {
 
 constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 
-// Exclusive scan of one int per thread over the 1024-thread block.
-// `wsum` is LDS scratch of >= 17 ints; returns the exclusive prefix and
-// writes the block total to *total (every thread sees it).
+// Exclusive scan of one int per thread over an NT-thread block.
+// `wsum` is LDS scratch of >= NT / 64 + 1 ints; returns the exclusive prefix
+// and writes the block total to *total (every thread sees it).
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int *total) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -41,24 +43,27 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int *total
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int w = (lane < kPlanThreads / 64) ? wsum[lane] : 0;
+    int w = (lane < NT / 64) ? wsum[lane] : 0;
     int inc = w;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       int y = __shfl_up(inc, o, 64);
       if (lane >= o) inc += y;
     }
-    if (lane < kPlanThreads / 64) wsum[lane] = inc - w;
-    if (lane == kPlanThreads / 64 - 1) wsum[kPlanThreads / 64] = inc;
+    if (lane < NT / 64) wsum[lane] = inc - w;
+    if (lane == NT / 64 - 1) wsum[NT / 64] = inc;
   }
   __syncthreads();
-  *total = wsum[kPlanThreads / 64];
+  *total = wsum[NT / 64];
   return x - v + wsum[wave];
 }
 
-__global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
-  __shared__ uint32_t keys[kPlanMaxRows];
-  __shared__ uint16_t sstart[kPlanMaxRows];
+template <int NT>
+__global__ __launch_bounds__(NT) void k_plan(PlanArgs a) {
+  // keys [n2] then segment starts [n2] (uint16), sized at launch
+  extern __shared__ __attribute__((aligned(16))) uint8_t plan_lds[];
+  uint32_t *keys = reinterpret_cast<uint32_t *>(plan_lds);
+  uint16_t *sstart = reinterpret_cast<uint16_t *>(plan_lds + ((size_t)4 << a.row_bits));
   __shared__ int wsum[32];
   __shared__ int cnt[4];
 
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   __syncthreads();
 
   // 1. classify
-  for (int m = tid; m < n2; m += kPlanThreads) {
+  for (int m = tid; m < n2; m += NT) {
     uint32_t key = kSentinel;
     if (m < M) {
       const int id = a.ids[m];
@@ -86,26 +91,32 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       } else if (id < -1 || id >= a.S) {
         atomicAdd(&cnt[0], 1);
       } else {
-        const int r = a.ranks[id];
-        if (r < 0 || r > a.R) {
-          atomicAdd(&cnt[1], 1);
-        } else {
-          bool ok = true;
-          if (a.page_table != nullptr) {
-            const int64_t bytes = (int64_t)r * a.bytes_per_rank;
-            const int64_t pages = (bytes + a.page_bytes - 1) / a.page_bytes;
-            if (pages > a.max_pages) ok = false;
-            for (int64_t j = 0; ok && j < pages; ++j) {
-              const int32_t p = a.page_table[(int64_t)id * a.max_pages + j];
-              if (p < 0 || (int64_t)p >= a.n_pages) ok = false;
+        // every slice's rank must be in range, then every slice's pages
+        bool rank_ok = true, page_ok = true;
+        for (int q = 0; q < a.n_slices; ++q) {
+          const PlanSlice &sl = a.sl[q];
+          const int r = sl.ranks[id];
+          if (r < 0 || r > sl.R) {
+            rank_ok = false;
+            continue;
+          }
+          if (sl.page_table != nullptr) {
+            const int64_t bytes = (int64_t)r * sl.bytes_per_rank;
+            const int64_t pages = (bytes + sl.page_bytes - 1) / sl.page_bytes;
+            if (pages > sl.max_pages) page_ok = false;
+            for (int64_t j = 0; page_ok && j < pages; ++j) {
+              const int32_t pg = sl.page_table[(int64_t)id * sl.max_pages + j];
+              if (pg < 0 || (int64_t)pg >= sl.n_pages) page_ok = false;
             }
           }
-          if (ok) {
-            key = ((uint32_t)id << a.row_bits) | (uint32_t)m;
-            atomicAdd(&cnt[3], 1);
-          } else {
-            atomicAdd(&cnt[2], 1);
-          }
+        }
+        if (!rank_ok) {
+          atomicAdd(&cnt[1], 1);
+        } else if (!page_ok) {
+          atomicAdd(&cnt[2], 1);
+        } else {
+          key = ((uint32_t)id << a.row_bits) | (uint32_t)m;
+          atomicAdd(&cnt[3], 1);
         }
       }
     }
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   // 2. bitonic sort, ascending, n2 keys (n2 a power of two)
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (n2 >> 1); i += kPlanThreads) {
+      for (int i = tid; i < (n2 >> 1); i += NT) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool up = (lo & size) == 0;
@@ -133,14 +144,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   // 3. segments
   const int n_ad = cnt[3];
   const uint32_t rmask = (1u << a.row_bits) - 1u;
-  const int chunk = (n2 + kPlanThreads - 1) / kPlanThreads;
+  const int chunk = (n2 + NT - 1) / NT;
   const int i0 = tid * chunk;
   int heads = 0;
   for (int i = i0; i < i0 + chunk; ++i) {
     if (i < n_ad) heads += (i == 0 || (keys[i] >> a.row_bits) != (keys[i - 1] >> a.row_bits));
   }
   int n_seg = 0;
-  int run = block_exclusive_scan(heads, wsum, &n_seg);
+  int run = block_exclusive_scan<NT>(heads, wsum, &n_seg);
   for (int i = i0; i < i0 + chunk; ++i) {
     if (i < n_ad) {
       const bool head = (i == 0 || (keys[i] >> a.row_bits) != (keys[i - 1] >> a.row_bits));
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   __syncthreads();
 
   // segment lengths and work-item counts
-  const int schunk = (n_seg + kPlanThreads - 1) / kPlanThreads;
+  const int schunk = (n_seg + NT - 1) / NT;
   const int s0 = tid * schunk;
   int ng = 0, ns = 0;
   for (int s = s0; s < s0 + schunk && s < n_seg; ++s) {
@@ -167,19 +178,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     ns += (len + kRowsPerSgmvItem - 1) / kRowsPerSgmvItem;
   }
   int n_items_g = 0, n_items_s = 0;
-  int og = block_exclusive_scan(ng, wsum, &n_items_g);
-  int os = block_exclusive_scan(ns, wsum, &n_items_s);
+  int og = block_exclusive_scan<NT>(ng, wsum, &n_items_g);
+  int os = block_exclusive_scan<NT>(ns, wsum, &n_items_s);
   for (int s = s0; s < s0 + schunk && s < n_seg; ++s) {
     const int st = sstart[s];
     const int len = ((s + 1 < n_seg) ? (int)sstart[s + 1] : n_ad) - st;
     const int ad = (int)(keys[st] >> a.row_bits);
-    const int r = a.ranks[ad];
     for (int p = 0; p < len; p += kRowsPerGatherItem) {
       Item it;
       it.adapter = ad;
       it.pos = st + p;
       it.nrows = min(kRowsPerGatherItem, len - p);
-      it.rank = r;
+      it.seg = s;
       items_g[og++] = it;
     }
     for (int p = 0; p < len; p += kRowsPerSgmvItem) {
@@ -187,7 +197,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       it.adapter = ad;
       it.pos = st + p;
       it.nrows = min(kRowsPerSgmvItem, len - p);
-      it.rank = r;
+      it.seg = s;
       items_s[os++] = it;
     }
   }
@@ -224,7 +234,13 @@ __global__ __launch_bounds__(256) void k_translate(AdapterRef ar, int32_t S, int
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, st, a);
+  // LDS sized to the batch (6 bytes per sort slot), so a small plan fits on
+  // a CU beside a GEMM workgroup; small batches use fewer waves
+  const size_t lds = (size_t)6 << a.row_bits;
+  if ((1 << a.row_bits) <= 1024)
+    hipLaunchKernelGGL(k_plan<256>, dim3(1), dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL(k_plan<kPlanThreads>, dim3(1), dim3(kPlanThreads), lds, st, a);
   return hipGetLastError();
 }
 

@@ -234,6 +234,7 @@ def custom(seed: int, M: int, k: int, d: int, ranks, max_rank: int, dtype=torch.
     w = _build("custom", 1000 + int(seed), dtype, M, k, {"out": d}, [max(r, 0) for r in ranks],
                alphas, max_rank, ids_fn, page_bytes=page_bytes)
     w.scales = (np.asarray(alphas, np.float32) / safe).astype(np.float32)
+    w.page_bytes = page_bytes or 4096
     return w
 
 

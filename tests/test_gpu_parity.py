@@ -322,3 +322,117 @@ def test_row_chunks_beyond_plan_limit(oracle_mod):
     rows = np.union1d(rows, np.arange(8180, 8210))
     ref = oracle_rows(oracle_mod, w, w.projections[0], rows)
     assert normwise(y[rows], ref) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# both kernel families (VALU gather, MFMA segments) on every bf16 workload
+# ---------------------------------------------------------------------------
+
+PATHS = [("gather", lr.PATH_GATHER), ("sgmv", lr.PATH_SGMV)]
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_paths_c1(oracle_mod, pname, path):
+    w = wl.c1_decode_bf16()
+    _check_full(oracle_mod, DevWorkload(w, w.projections[0]), "c1 " + pname, path=path)
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_paths_c2(oracle_mod, pname, path):
+    w = wl.c2_prefill_bf16()
+    _check_full(oracle_mod, DevWorkload(w, w.projections[0]), "c2 " + pname,
+                rows=sample_rows(w, 48), path=path)
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_paths_c3(oracle_mod, c3, pname, path):
+    _check_full(oracle_mod, DevWorkload(c3, c3.proj("q")), "c3 q " + pname,
+                rows=sample_rows(c3, 40), path=path)
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_paths_c4_pool(oracle_mod, c4, pname, path):
+    _check_full(oracle_mod, DevWorkload(c4, c4.projections[0], pooled=True), "c4 pool " + pname,
+                rows=sample_rows(c4, 40), path=path)
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_paths_small(oracle_mod, pname, path):
+    for w, pooled in ((wl.u1_scales(dtype=torch.bfloat16), False),
+                      (wl.u2_pages(dtype=torch.bfloat16), True),
+                      (wl.custom(seed=41, M=300, k=264, d=130, ranks=[1, 3, 8, 17, 33, 64],
+                                 max_rank=64), False),
+                      (wl.custom(seed=42, M=1500, k=512, d=96, ranks=[8, 40, 16], max_rank=40,
+                                 sorted_ids=True), False)):
+        _check_full(oracle_mod, DevWorkload(w, w.projections[0], pooled=pooled),
+                    "%s %s" % (w.name, pname), path=path)
+
+
+def test_sgmv_unsupported_combinations():
+    say("sgmv unsupported")
+    w = wl.custom(seed=3, M=32, k=64, d=32, ranks=[4, 4], max_rank=4, dtype=torch.float32)
+    dw = DevWorkload(w, w.projections[0])
+    with pytest.raises(lr.LoraError) as e:
+        dw.run(path=lr.PATH_SGMV)
+    assert e.value.status == 8
+    w = wl.custom(seed=4, M=32, k=64, d=32, ranks=[4, 100], max_rank=128)
+    dw = DevWorkload(w, w.projections[0])
+    with pytest.raises(lr.LoraError) as e:
+        dw.run(path=lr.PATH_SGMV)
+    assert e.value.status == 8
+    dw.run(path=lr.PATH_AUTO)  # falls to the VALU kernels
+
+
+# ---------------------------------------------------------------------------
+# several projections in one call
+# ---------------------------------------------------------------------------
+
+def _stacked(ws_list):
+    return torch.cat([w for w in ws_list], dim=0).contiguous()
+
+
+@pytest.mark.parametrize("pname,path", [("auto", lr.PATH_AUTO)] + PATHS,
+                         ids=["auto", "gather", "sgmv"])
+def test_sliced_c3_q_and_v(oracle_mod, c3, pname, path):
+    say("sliced c3 q+v " + pname)
+    pq, pv = c3.proj("q"), c3.proj("v")
+    dq, dv = DevWorkload(c3, pq), DevWorkload(c3, pv)
+    W = _stacked([dq.W, dv.W])
+    slices = [lr.Slice(pq.d, dq.ad, dq.scales), lr.Slice(pv.d, dv.ad, dv.scales)]
+    y = lr.lora_linear_sliced(dq.x, W, slices, dq.ids, path=path)
+    torch.cuda.synchronize()
+    base = lr.lora_gemm(dq.x, W)
+    torch.cuda.synchronize()
+    rows = sample_rows(c3, 40)
+    yq = y[:, :pq.d].double().cpu().numpy()
+    yv = y[:, pq.d:].double().cpu().numpy()
+    for name, got, p in (("q", yq, pq), ("v", yv, pv)):
+        ref = oracle_rows(oracle_mod, c3, p, rows)
+        err = normwise(got[rows], ref)
+        say("  %s normwise error %.3g" % (name, err))
+        assert err <= 2e-2
+    none = np.flatnonzero(c3.ids < 0)
+    assert torch.equal(y[none], base[none])
+    # same as the q projection alone, to the bf16 tolerance
+    y1 = dq.run(path=path)
+    assert normwise(yq, y1.double().cpu().numpy()) <= 1e-2
+
+
+def test_sliced_mixed_storage_and_rank_zero(oracle_mod):
+    """Slice 0 in slots, slice 1 in a paged pool where adapter 2 has rank 0
+    (it does not touch that projection)."""
+    say("sliced mixed storage")
+    M, k = 200, 256
+    w0 = wl.custom(seed=61, M=M, k=k, d=96, ranks=[8, 16, 4, 32], max_rank=32)
+    w1 = wl.custom(seed=61, M=M, k=k, d=40, ranks=[4, 8, 0, 16], max_rank=16)
+    w1.x, w1.ids = w0.x, w0.ids
+    d0 = DevWorkload(w0, w0.projections[0])
+    d1 = DevWorkload(w1, w1.projections[0], pooled=True, page_bytes=4096)
+    W = _stacked([d0.W, d1.W])
+    slices = [lr.Slice(96, d0.ad, d0.scales), lr.Slice(40, d1.ad, d1.scales)]
+    for path in (lr.PATH_GATHER, lr.PATH_SGMV):
+        y = lr.lora_linear_sliced(d0.x, W, slices, d0.ids, path=path)
+        torch.cuda.synchronize()
+        y = y.double().cpu().numpy()
+        assert normwise(y[:, :96], oracle_rows(oracle_mod, w0, w0.projections[0])) <= 2e-2
+        assert normwise(y[:, 96:], oracle_rows(oracle_mod, w1, w1.projections[0])) <= 2e-2
