@@ -50,9 +50,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets")
     ap.add_argument("--path", default="auto", choices=["auto", "gather", "sgmv"])
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="write profiles/ summaries from a rocprofv3 run whose trace/, fetch/, "
+                         "write/, cfetch/, cwrite/ output directories are under DIR, and exit")
+    ap.add_argument("--profiled-command", default="python3 bench.py --no-cpu-baseline --steps 20",
+                    help="the bench command the profiling run used (recorded in the summary)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 5 times (scales the FETCH_SIZE / "
                          "WRITE_SIZE counters of a profiling run) and exit")
@@ -76,6 +81,13 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.summarize_profiles:
+        from lora_row_adapter_amd import profile_tools
+        res = profile_tools.summarize(args.summarize_profiles, os.path.join(ROOT, "profiles"),
+                                      args.profiled_command, 256, GEMM_SOURCE,
+                                      "c3_proj70b_bf16 q+v, 512 rows")
+        print(json.dumps({k: v for k, v in res.items() if k != "kernel_trace"}, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is row-independent and this build runs on a "
