@@ -107,29 +107,45 @@ struct SliceRef {
   int64_t col0;
 };
 
-// Index of the fp32 shrink partial of (sorted position p, slice s, rank j,
-// k split q).  The split index is innermost so a reader sums one contiguous
-// run of kMaxKSplit floats.
-__device__ __forceinline__ int64_t tpart_index(int64_t p, int s, int j, int q, int n_slices,
-                                               int R) {
-  return (((p * n_slices + s) * R + j) * kMaxKSplit) + q;
+// Index of the fp32 shrink partial of (k split q, sorted position p, slice s,
+// rank j): one [rows][slices][R] block per split, so a reader that needs the
+// item's rows for every split reads ksplit contiguous runs.
+__device__ __forceinline__ int64_t tpart_index(int q, int64_t p, int s, int j, int64_t rows,
+                                               int n_slices, int R) {
+  return ((q * rows + p) * n_slices + s) * (int64_t)R + j;
 }
 
-// Sum of the k-split partials of (p, s, j): one 64-byte run, read as four
-// 16-byte vectors; slots past `ksplit` (never written) are masked out.
-__device__ __forceinline__ float tpart_sum(const float *tpart, int64_t p, int s, int j, int ksplit,
-                                           int n_slices, int R) {
-  const float4 *q4 = reinterpret_cast<const float4 *>(tpart + tpart_index(p, s, j, 0, n_slices, R));
-  float v = 0.f;
+// t[p, s, j..j+3] = the four k-split sums, in split order (R % 4 == 0).
+__device__ __forceinline__ float4 tpart_sum4(const float *tpart, int64_t p, int s, int j,
+                                             int ksplit, int64_t rows, int n_slices, int R) {
+  float4 v[kMaxKSplit];
 #pragma unroll
-  for (int i = 0; i < kMaxKSplit / 4; ++i) {
-    const float4 f = q4[i];
-    v += (4 * i + 0 < ksplit) ? f.x : 0.f;
-    v += (4 * i + 1 < ksplit) ? f.y : 0.f;
-    v += (4 * i + 2 < ksplit) ? f.z : 0.f;
-    v += (4 * i + 3 < ksplit) ? f.w : 0.f;
+  for (int q = 0; q < kMaxKSplit; ++q)
+    v[q] = q < ksplit ? *reinterpret_cast<const float4 *>(
+                            tpart + tpart_index(q, p, s, j, rows, n_slices, R))
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 acc = v[0];
+#pragma unroll
+  for (int q = 1; q < kMaxKSplit; ++q) {
+    acc.x += v[q].x;
+    acc.y += v[q].y;
+    acc.z += v[q].z;
+    acc.w += v[q].w;
   }
-  return v;
+  return acc;
+}
+
+// Scalar form for any R.
+__device__ __forceinline__ float tpart_sum1(const float *tpart, int64_t p, int s, int j,
+                                            int ksplit, int64_t rows, int n_slices, int R) {
+  float v[kMaxKSplit];
+#pragma unroll
+  for (int q = 0; q < kMaxKSplit; ++q)
+    v[q] = q < ksplit ? tpart[tpart_index(q, p, s, j, rows, n_slices, R)] : 0.f;
+  float acc = v[0];
+#pragma unroll
+  for (int q = 1; q < kMaxKSplit; ++q) acc += v[q];
+  return acc;
 }
 
 }  // namespace lora

@@ -199,8 +199,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_pipe(PipeArgs p) {
   static_assert(STAGES * STAGE_BYTES >= ECH * CLD * 2, "epilogue fits");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
-  const int nblk = p.tiles_m * p.tiles_n;
   const int b = blockIdx.x;
+  const int nblk = p.tiles_m * p.tiles_n;
   const int t = ((nblk & 7) == 0) ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
   const int tm = t % p.tiles_m;
   const int tn = t / p.tiles_m;

@@ -15,7 +15,7 @@ struct WsLayout {
   int64_t seg_cap = 0;
   int64_t items_g_cap = 0;
   int64_t items_s_cap = 0;
-  int32_t R = 0;
+  int32_t R = 0;  // fp32 partial row width: max rank rounded up to 4
   size_t hdr = 0, perm = 0, seg_adapter = 0, seg_start = 0, seg_len = 0;
   size_t items_g = 0, items_s = 0, tpart = 0, total = 0;
 };
@@ -52,6 +52,7 @@ struct LoraArgs {
   int64_t ldx;
   void *y;
   int64_t ldy;
+  int32_t y_vec;    // y base 16-byte aligned and ldy a multiple of 16 bytes
   int32_t n_slices;
   int32_t R;        // max rank over slices (partials row width)
   SliceRef sl[kMaxSlices];
@@ -66,11 +67,13 @@ hipError_t launch_plan(const PlanArgs &a, hipStream_t st);
 hipError_t launch_translate(const AdapterRef &ar, int32_t S, int64_t n_pages,
                             const int32_t *adapter, const int64_t *off, int64_t n,
                             int64_t *phys, hipStream_t st);
+// Base GEMM y = x W^T (bf16 operands: MFMA tiles; fp32: VALU).
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, hipStream_t st);
 hipError_t launch_shrink_gather(const LoraArgs &a, hipStream_t st);
 hipError_t launch_expand_gather(const LoraArgs &a, hipStream_t st);
-hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, hipStream_t st);
+hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_slice,
+                              hipStream_t st);
 hipError_t launch_expand_sgmv(const LoraArgs &a, int rows_per_item, hipStream_t st);
 constexpr int kMaxRankMfma = 64;
 

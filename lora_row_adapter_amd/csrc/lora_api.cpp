@@ -14,12 +14,16 @@
 
 namespace lora {
 
+// MFMA shrink: one workgroup per slice (more parallelism) rather than one
+// for all slices (x read once).
+constexpr bool kShrinkPerSlice = true;
+
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(int64_t rows, int32_t S, int32_t R, int32_t n_slices) {
   WsLayout L;
   L.rows = std::max<int64_t>(1, rows);
-  L.R = R;
+  L.R = (std::max<int32_t>(R, 1) + 3) & ~3;  // partial row width (float4 runs)
   L.seg_cap = std::max<int64_t>(1, std::min<int64_t>(L.rows, S));
   L.items_g_cap = (L.rows + kRowsPerGatherItem - 1) / kRowsPerGatherItem + L.seg_cap;
   L.items_s_cap = (L.rows + kRowsPerSgmvItem - 1) / kRowsPerSgmvItem + L.seg_cap;
@@ -36,7 +40,7 @@ WsLayout ws_layout(int64_t rows, int32_t S, int32_t R, int32_t n_slices) {
   L.seg_len = take((size_t)L.seg_cap * sizeof(int32_t));
   L.items_g = take((size_t)L.items_g_cap * sizeof(Item));
   L.items_s = take((size_t)L.items_s_cap * sizeof(Item));
-  L.tpart = take((size_t)kMaxKSplit * L.rows * n_slices * R * sizeof(float));
+  L.tpart = take((size_t)kMaxKSplit * L.rows * n_slices * L.R * sizeof(float));
   L.total = off;
   return L;
 }
@@ -64,7 +68,10 @@ int begin(int c, hipStream_t st) {
     ev1.resize(kRing);
     cls.resize(kRing);
     for (int i = 0; i < kRing; ++i) {
-      if (hipEventCreate(&ev0[i]) != hipSuccess || hipEventCreate(&ev1[i]) != hipSuccess) {
+      // timing only: no system-scope fence (it would write back caches and
+      // perturb the work being timed)
+      if (hipEventCreateWithFlags(&ev0[i], hipEventDisableSystemFence) != hipSuccess ||
+          hipEventCreateWithFlags(&ev1[i], hipEventDisableSystemFence) != hipSuccess) {
         ev0.clear();
         ev1.clear();
         return -1;
@@ -90,7 +97,9 @@ void end(int i, hipStream_t st) {
 // Side stream for the plan: the plan depends only on the ids, the GEMM only
 // on x and W, so the plan runs beside the GEMM and the caller's stream waits
 // for it before the shrink.  One non-blocking stream (default priority) and
-// a ring of events per device, created on first use and kept.
+// a ring of events per device, created on first use and kept.  (Launching
+// the GEMM unordered behind the plan on the caller's stream was measured not
+// to overlap them.)
 // ---------------------------------------------------------------------------
 namespace side {
 constexpr int kMaxDev = 64;
@@ -113,7 +122,11 @@ bool get(hipStream_t *s, hipEvent_t *fork, hipEvent_t *join) {
     D.tried = true;
     if (hipStreamCreateWithFlags(&D.s, hipStreamNonBlocking) != hipSuccess) return false;
     for (int i = 0; i < kEvents; ++i)
-      if (hipEventCreateWithFlags(&D.ev[i], hipEventDisableTiming) != hipSuccess) return false;
+      // device-scope release: the waiting stream is on the same device (a
+      // system-scope release would write caches back on every record)
+      if (hipEventCreateWithFlags(&D.ev[i], hipEventDisableTiming | hipEventReleaseToDevice) !=
+          hipSuccess)
+        return false;
     D.ok = true;
   }
   if (!D.ok) return false;
@@ -124,6 +137,7 @@ bool get(hipStream_t *s, hipEvent_t *fork, hipEvent_t *join) {
   return true;
 }
 }  // namespace side
+
 
 template <typename F>
 static hipError_t timed(int c, hipStream_t st, F &&launch) {
@@ -275,9 +289,9 @@ lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, con
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
-static lora_status_t run_plan(int64_t M, int64_t k, lora_dtype_t dtype, int32_t n_slices,
-                              const lora_slice_t *slices, const int32_t *ids, uint8_t *ws,
-                              const WsLayout &L, hipStream_t st) {
+static PlanArgs make_plan_args(int64_t M, int64_t k, lora_dtype_t dtype, int32_t n_slices,
+                               const lora_slice_t *slices, const int32_t *ids, uint8_t *ws,
+                               const WsLayout &L) {
   PlanArgs p{};
   p.ids = ids;
   p.M = (int32_t)M;
@@ -300,6 +314,13 @@ static lora_status_t run_plan(int64_t M, int64_t k, lora_dtype_t dtype, int32_t 
   }
   p.ws = ws;
   p.L = L;
+  return p;
+}
+
+static lora_status_t run_plan(int64_t M, int64_t k, lora_dtype_t dtype, int32_t n_slices,
+                              const lora_slice_t *slices, const int32_t *ids, uint8_t *ws,
+                              const WsLayout &L, hipStream_t st) {
+  const PlanArgs p = make_plan_args(M, k, dtype, n_slices, slices, ids, ws, L);
   hipError_t e = timed(LORA_K_PLAN, st, [&] { return launch_plan(p, st); });
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -395,6 +416,7 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
   a.k = k;
   a.ldx = ldx;
   a.ldy = ldy;
+  a.y_vec = ((uintptr_t)y % 16 == 0 && (ldy * eb) % 16 == 0) ? 1 : 0;
   a.n_slices = n_slices;
   a.R = R;
   a.ws = ws;
@@ -414,23 +436,6 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
     const WsLayout L = ws_layout(Mc, S, R, n_slices);
     const uint8_t *xc = (const uint8_t *)x + c0 * ldx * eb;
     uint8_t *yc = (uint8_t *)y + c0 * ldy * eb;
-    hipStream_t ps = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-    const bool fork = !(flags & LORA_FLAG_REUSE_PLAN) && side::get(&ps, &ev_fork, &ev_join);
-    if (!(flags & LORA_FLAG_REUSE_PLAN)) {
-      if (fork) {
-        if (hipEventRecord(ev_fork, st) != hipSuccess || hipStreamWaitEvent(ps, ev_fork, 0) != hipSuccess)
-          return LORA_ERR_HIP;
-      }
-      s = run_plan(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L, fork ? ps : st);
-      if (s != LORA_OK) return s;
-      if (fork && hipEventRecord(ev_join, ps) != hipSuccess) return LORA_ERR_HIP;
-    }
-    hipError_t e = timed(LORA_K_GEMM, st, [&] {
-      return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, st);
-    });
-    if (e != hipSuccess) return LORA_ERR_HIP;
-    if (fork && hipStreamWaitEvent(st, ev_join, 0) != hipSuccess) return LORA_ERR_HIP;
 
     a.x = xc;
     a.y = yc;
@@ -446,19 +451,48 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
 
     // k splits: aim for ~600 shrink workgroups on the 256 CUs (measured
     // best for decode batches: more splits add partials for the expand to
-    // sum, fewer leave CUs idle)
+    // sum, fewer leave CUs idle).  The MFMA shrink covers all slices in one
+    // workgroup; the gather shrink takes one per slice and 16-rank block.
     const int64_t est_items = (Mc + rpi - 1) / rpi + std::min<int64_t>(segs, 64);
-    const int64_t jblk = use_mfma ? 1 : (R + 15) / 16;
-    const int64_t per_split =
-        std::max<int64_t>(1, est_items * n_slices * (use_mfma ? 1 : std::min<int64_t>(jblk, 2)));
+    const int64_t jblk = (R + 15) / 16;
+    const bool per_slice = kShrinkPerSlice;
+    const int64_t per_split = std::max<int64_t>(
+        1, use_mfma ? est_items * (per_slice ? n_slices : 1)
+                    : est_items * n_slices * std::min<int64_t>(jblk, 2));
     int64_t ks = std::max<int64_t>(1, std::min<int64_t>(kMaxKSplit, (600 + per_split - 1) / per_split));
     int64_t kchunk = (k + ks - 1) / ks;
     kchunk = (kchunk + 255) / 256 * 256;
     ks = (k + kchunk - 1) / kchunk;
     a.ksplit = (int32_t)ks;
     a.kchunk = kchunk;
+
+    // The plan needs only the ids, the GEMM only x and W: with a side
+    // stream the plan runs beside the GEMM and the caller's stream waits
+    // for it before the shrink.  (A shrink on the side stream as well gets
+    // only the GEMM's leftover CU resources and finishes later than after
+    // it.)  Later calls on the caller's stream are ordered after this call
+    // by the fork event, so the workspace is never rewritten while read.
+    hipStream_t ps = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    const bool reuse = (flags & LORA_FLAG_REUSE_PLAN) != 0;
+    const bool fork = !reuse && side::get(&ps, &ev_fork, &ev_join);
+    if (!reuse) {
+      if (fork) {
+        if (hipEventRecord(ev_fork, st) != hipSuccess || hipStreamWaitEvent(ps, ev_fork, 0) != hipSuccess)
+          return LORA_ERR_HIP;
+      }
+      s = run_plan(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L, fork ? ps : st);
+      if (s != LORA_OK) return s;
+      if (fork && hipEventRecord(ev_join, ps) != hipSuccess) return LORA_ERR_HIP;
+    }
+    hipError_t e = timed(LORA_K_GEMM, st, [&] {
+      return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, st);
+    });
+    if (e != hipSuccess) return LORA_ERR_HIP;
+    if (fork && hipStreamWaitEvent(st, ev_join, 0) != hipSuccess) return LORA_ERR_HIP;
+
     if (use_mfma) {
-      e = timed(LORA_K_SGMV_SHRINK, st, [&] { return launch_shrink_sgmv(a, rpi, st); });
+      e = timed(LORA_K_SGMV_SHRINK, st, [&] { return launch_shrink_sgmv(a, rpi, per_slice, st); });
       if (e != hipSuccess) return LORA_ERR_HIP;
       e = timed(LORA_K_SGMV_EXPAND, st, [&] { return launch_expand_sgmv(a, rpi, st); });
       if (e != hipSuccess) return LORA_ERR_HIP;

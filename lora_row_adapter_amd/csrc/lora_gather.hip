@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void k_shrink_gather(LoraArgs a) {
   const int jj = lane & 15;
   if (rowv[rr] && jj < nj) {
     const int64_t p = it.pos + wave * RPW + rr;
-    tpart[tpart_index(p, slice, j0 + jj, blockIdx.z, a.n_slices, a.R)] = sum;
+    tpart[tpart_index(blockIdx.z, p, slice, j0 + jj, a.L.rows, a.n_slices, a.L.R)] = sum;
   }
 }
 
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int EB = Elem<DT>::bytes;
   constexpr int VEC = 16 / EB;  // elements per 16-byte vector
-  __shared__ float ts[kRowsPerGatherItem * kMaxRank];
+  __shared__ __attribute__((aligned(16))) float ts[kRowsPerGatherItem * kMaxRank];
 
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
   const int item = blockIdx.x;
@@ -205,10 +205,16 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
   const float *tpart = reinterpret_cast<const float *>(a.ws + a.L.tpart);
   const int tid = threadIdx.x;
 
-  for (int idx = tid; idx < nr * r; idx += 256) {
-    const int row = idx / r;
-    const int j = idx - row * r;
-    ts[row * kMaxRank + j] = tpart_sum(tpart, it.pos + row, slice, j, a.ksplit, a.n_slices, a.R);
+  const int r4 = (r + 3) >> 2;  // float4 runs per row
+  for (int idx = tid; idx < nr * r4; idx += 256) {
+    const int row = idx / r4;
+    const int j = (idx - row * r4) * 4;
+    float4 v = tpart_sum4(tpart, it.pos + row, slice, j, a.ksplit, a.L.rows, a.n_slices, a.L.R);
+    // entries past the rank are never written by the shrink
+    if (j + 1 >= r) v.y = 0.f;
+    if (j + 2 >= r) v.z = 0.f;
+    if (j + 3 >= r) v.w = 0.f;
+    *reinterpret_cast<float4 *>(&ts[row * kMaxRank + j]) = v;
   }
   __syncthreads();
 

@@ -12,12 +12,15 @@
 // one adapter's segment.  bf16 only (the matrix cores' operand type).
 //
 // shrink: t[p, j] = sum_k A_s[j, k] x[perm[p], k]
-//   grid (item, slice, k split).  16 x 16 output blocks (rows x ranks) on
-//   v_mfma_f32_16x16x32_bf16; x rows are gathered through perm straight into
-//   the A operand (16 bytes per lane), A_s rows into the B operand.  The 4
-//   waves take alternate 32-wide k steps of the split; their partial blocks
-//   are summed in wave order through LDS.  Output: fp32 partials, one per k
-//   split (summed in split order by the expand).
+//   grid (item, slice or all slices, k split).  A workgroup covers the
+//   16-rank blocks of one slice, or of every slice (then each x row is
+//   fetched once for all projections, with fewer workgroups).
+//   16 x 16 output blocks (rows x ranks) on v_mfma_f32_16x16x32_bf16; x rows
+//   are gathered through perm straight into the A operand (16 bytes per
+//   lane), A_s rows into the B operand.  The 4 waves take alternate 32-wide k
+//   steps of the split; their partial blocks are summed in wave order through
+//   LDS.  Output: fp32 partials, one per k split (summed in split order by
+//   the expand).
 // expand: y[perm[p], n] += scale_s * sum_j B_s[n, j] t[p, j]
 //   grid (item, 256-column block of any slice).  t (the sum of the k-split
 //   partials, in split order) is split into bf16 hi + lo parts (t = hi + lo to ~16 mantissa
@@ -42,31 +45,179 @@ __device__ __forceinline__ bf16x8_t zero8() {
   return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
 }
 
-template <int RB>
-__global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
+// Row of A_s as seen by one lane: a 16-rank block of one slice.  For slot
+// storage `base` is the row start; for a pool each 16-byte vector goes
+// through the page table (a vector never crosses a page).
+struct ARow {
+  const uint8_t *base;  // slots: &A_s[j][0]; pool: pool base
+  const int32_t *pt;    // pool: page-table row of the adapter; slots: nullptr
+  int64_t off;          // pool: logical byte offset of A_s[j][0]
+  int32_t shift;
+  int64_t mask;
+};
+
+__device__ __forceinline__ ARow make_arow(const AdapterRef &ar, int s, int64_t j) {
+  ARow w;
+  if (!ar.pooled) {
+    w.base = ar.A + ((int64_t)s * ar.max_rank + j) * ar.k * ar.elem_bytes;
+    w.pt = nullptr;
+    w.off = 0;
+  } else {
+    w.base = ar.pool;
+    w.pt = ar.page_table + (int64_t)s * ar.max_pages;
+    w.off = j * ar.k * ar.elem_bytes;
+  }
+  w.shift = ar.page_shift;
+  w.mask = ar.page_bytes - 1;
+  return w;
+}
+
+__device__ __forceinline__ const uint8_t *arow_ptr(const ARow &w, int64_t kk) {
+  if (w.pt == nullptr) return w.base + kk * 2;
+  const int64_t off = w.off + kk * 2;
+  return w.base + ((int64_t)w.pt[off >> w.shift] << w.shift) + (off & w.mask);
+}
+
+// The item's rank blocks over all slices, in slice order: block v is
+// (slice, 16-rank block) with 16 * block < r_slice.  Returns the count and,
+// for v, its slice / block / rank.
+__device__ __forceinline__ int vblock_count(const LoraArgs &a, int adapter) {
+  int n = 0;
+  for (int q = 0; q < a.n_slices; ++q) n += (a.sl[q].ranks[adapter] + 15) >> 4;
+  return n;
+}
+__device__ __forceinline__ void vblock_find(const LoraArgs &a, int adapter, int v, int &slice,
+                                            int &jb, int &r) {
+  slice = 0;
+  jb = v;
+  r = a.sl[0].ranks[adapter];
+  for (int q = 0; q + 1 < a.n_slices; ++q) {
+    const int nb = (r + 15) >> 4;
+    if (jb < nb) break;
+    jb -= nb;
+    slice = q + 1;
+    r = a.sl[q + 1].ranks[adapter];
+  }
+}
+
+// Rank blocks [v0, v0 + G) of one item over one k split: MFMA partial
+// blocks per wave (alternate 32-wide k steps), summed in wave order through
+// LDS, written as this split's fp32 partials.
+template <int RB, int G, int U>
+__device__ __forceinline__ void shrink_blocks(const LoraArgs &a, const Item &it, int v0, int nvb,
+                                              int64_t kbeg, int64_t kend,
+                                              const int64_t (&xoff)[RB / 16],
+                                              const bool (&xv)[RB / 16],
+                                              f32x4_t (*red)[4][64]) {
   constexpr int RBK = RB / 16;
-  __shared__ f32x4_t red[4][RBK * 4][64];
-
-  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
-  const int item = blockIdx.x;
-  if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
-  const Item it =
-      reinterpret_cast<const Item *>(a.ws + (RB == 16 ? a.L.items_g : a.L.items_s))[item];
-  const int slice = blockIdx.y;
-  const SliceRef &sl = a.sl[slice];
-  const int r = sl.ranks[it.adapter];
-  if (r == 0) return;
-  const int64_t kbeg = (int64_t)blockIdx.z * a.kchunk;
-  if (kbeg >= a.k) return;
-  const int64_t kend = min(a.k, kbeg + a.kchunk);
-  const int32_t *perm = reinterpret_cast<const int32_t *>(a.ws + a.L.perm);
-  float *tpart = reinterpret_cast<float *>(a.ws + a.L.tpart);
-  const uint16_t *xb = reinterpret_cast<const uint16_t *>(a.x);
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int kl = (lane >> 4) * 8;
+  const uint16_t *xb = reinterpret_cast<const uint16_t *>(a.x);
+
+  ARow arow[G];
+  bool jv[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    jv[g] = false;
+    arow[g] = ARow{nullptr, nullptr, 0, 0, 0};
+    if (v0 + g < nvb) {
+      int slice, jb, r;
+      vblock_find(a, it.adapter, v0 + g, slice, jb, r);
+      const int j = jb * 16 + (lane & 15);
+      jv[g] = j < r;
+      arow[g] = make_arow(a.sl[slice].ar, it.adapter, jv[g] ? j : 0);
+    }
+  }
+
+  f32x4_t acc[RBK][G];
+#pragma unroll
+  for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[rb][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // U k steps per round: all their loads are issued before their MFMAs
+  for (int64_t kb0 = kbeg + wave * 32; kb0 < kend; kb0 += 128 * U) {
+    bf16x8_t xf[U][RBK], af[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t kc = kb0 + 128 * u + kl;
+      const bool kin = kc < kend;
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb)
+        xf[u][rb] = (xv[rb] && kin) ? ld16(xb + xoff[rb] + kc) : zero8();
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        af[u][g] = (jv[g] && kin) ? ld16(arow_ptr(arow[g], kc)) : zero8();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (v0 + g < nvb)
+            acc[rb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][rb], af[u][g], acc[rb][g], 0, 0, 0);
+  }
+
+  float *tpart = reinterpret_cast<float *>(a.ws + a.L.tpart);
+  // four output blocks per round through LDS; wave w sums block w
+#pragma unroll
+  for (int c0 = 0; c0 < RBK * G; c0 += 4) {
+    if (v0 + (c0 % G) >= nvb) continue;  // uniform: the whole chunk is past the end
+    __syncthreads();  // the previous round's reads of red are done
+#pragma unroll
+    for (int b = 0; b < 4; ++b) red[wave][b][lane] = acc[(c0 + b) / G][(c0 + b) % G];
+    __syncthreads();
+    const int blk = c0 + wave;
+    const int rb = blk / G;
+    const int g = blk % G;
+    if (v0 + g < nvb) {
+      int slice, jb, r;
+      vblock_find(a, it.adapter, v0 + g, slice, jb, r);
+      const f32x4_t sum = ((red[0][wave][lane] + red[1][wave][lane]) + red[2][wave][lane]) +
+                          red[3][wave][lane];
+      const int j = jb * 16 + (lane & 15);
+      if (j < r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = rb * 16 + ((lane >> 4) << 2) + i;
+          if (row < it.nrows)
+            tpart[tpart_index(blockIdx.z, it.pos + row, slice, j, a.L.rows, a.n_slices, a.L.R)] =
+                sum[i];
+        }
+      }
+    }
+  }
+}
+
+// grid (item, k split): x rows are loaded once for every slice's A.
+template <int RB>
+__global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
+  constexpr int RBK = RB / 16;
+  __shared__ f32x4_t red[4][4][64];
+
+  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
+  const int item = blockIdx.x;
+  // the item slot exists up to the list's capacity: read it beside the count
+  const Item it =
+      reinterpret_cast<const Item *>(a.ws + (RB == 16 ? a.L.items_g : a.L.items_s))[item];
+  if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
+  // grid.y == 1: every slice's rank blocks (x rows read once for all);
+  // grid.y == n_slices: slice blockIdx.y's blocks only (more workgroups)
+  int vlo = 0, vhi = vblock_count(a, it.adapter);
+  if (gridDim.y > 1) {
+    vlo = 0;
+    for (int q = 0; q < (int)blockIdx.y; ++q) vlo += (a.sl[q].ranks[it.adapter] + 15) >> 4;
+    vhi = vlo + ((a.sl[blockIdx.y].ranks[it.adapter] + 15) >> 4);
+  }
+  if (vhi == vlo) return;
+  const int64_t kbeg = (int64_t)blockIdx.z * a.kchunk;
+  if (kbeg >= a.k) return;
+  const int64_t kend = min(a.k, kbeg + a.kchunk);
+  const int32_t *perm = reinterpret_cast<const int32_t *>(a.ws + a.L.perm);
+  const int lane = threadIdx.x & 63;
 
   int64_t xoff[RBK];
   bool xv[RBK];
@@ -77,68 +228,14 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
     xoff[rb] = xv[rb] ? (int64_t)perm[it.pos + row] * a.ldx : 0;
   }
 
-  const int JB = (r + 15) / 16;
-  for (int jg = 0; jg < JB; jg += 4) {
-    f32x4_t acc[RBK][4];
-#pragma unroll
-    for (int rb = 0; rb < RBK; ++rb)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) acc[rb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    int jrow[4];
-    bool jv[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      jrow[jb] = (jg + jb) * 16 + (lane & 15);
-      jv[jb] = jrow[jb] < r;
-    }
-    // U k-steps per round: all their loads are issued before their MFMAs
-    constexpr int U = 4;
-    for (int64_t kb0 = kbeg + wave * 32; kb0 < kend; kb0 += 128 * U) {
-      bf16x8_t xf[U][RBK], af[U][4];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t kc = kb0 + 128 * u + kl;
-        const bool kin = kc < kend;
-#pragma unroll
-        for (int rb = 0; rb < RBK; ++rb)
-          xf[u][rb] = (xv[rb] && kin) ? ld16(xb + xoff[rb] + kc) : zero8();
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-          af[u][jb] = (jv[jb] && kin) ? ld16(adapter_a_ptr(sl.ar, it.adapter, r, jrow[jb], kc))
-                                      : zero8();
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int rb = 0; rb < RBK; ++rb)
-#pragma unroll
-          for (int jb = 0; jb < 4; ++jb)
-            if (jg + jb < JB)
-              acc[rb][jb] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][rb], af[u][jb], acc[rb][jb], 0, 0, 0);
-    }
-    __syncthreads();  // the previous group's reads of red are done
-#pragma unroll
-    for (int rb = 0; rb < RBK; ++rb)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) red[wave][rb * 4 + jb][lane] = acc[rb][jb];
-    __syncthreads();
-    for (int e = tid; e < RBK * 4 * 64; e += 256) {
-      const int blk = e >> 6;
-      const int ln = e & 63;
-      const int rb = blk >> 2;
-      const int jb = blk & 3;
-      if (jg + jb >= JB) continue;
-      const f32x4_t s = ((red[0][blk][ln] + red[1][blk][ln]) + red[2][blk][ln]) + red[3][blk][ln];
-      const int j = (jg + jb) * 16 + (ln & 15);
-      if (j >= r) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rb * 16 + ((ln >> 4) << 2) + i;
-        if (row < it.nrows)
-          tpart[tpart_index(it.pos + row, slice, j, blockIdx.z, a.n_slices, a.R)] = s[i];
-      }
-    }
+  // block groups sized so that few blocks keep several k steps of loads
+  // in flight; up to 8 blocks (two projections of rank 64) share one read
+  // of the x rows, more take another pass over them
+  if (vhi - vlo <= 4) {
+    shrink_blocks<RB, 4, 4>(a, it, vlo, vhi, kbeg, kend, xoff, xv, red);
+  } else {
+    for (int v0 = vlo; v0 < vhi; v0 += 8)
+      shrink_blocks<RB, 8, RB == 16 ? 2 : 1>(a, it, v0, vhi, kbeg, kend, xoff, xv, red);
   }
 }
 
@@ -146,14 +243,19 @@ template <int RB>
 __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   constexpr int RBK = RB / 16;
   constexpr int KP = RMAX_MFMA + 8;  // padded LDS row (bf16)
+  constexpr int YLD = ECB + 4;       // transposed-output LDS row (fp32)
+  constexpr int YCH = 2 * RBK;       // 16-byte y chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t th[RB * KP];
   __shared__ __attribute__((aligned(16))) uint16_t tl[RB * KP];
+  __shared__ __attribute__((aligned(16))) float ys[16 * YLD];
 
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
   const int item = blockIdx.x;
-  if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
+  // the item slot exists up to the list's capacity, so it is read beside
+  // the count instead of after it
   const Item it =
       reinterpret_cast<const Item *>(a.ws + (RB == 16 ? a.L.items_g : a.L.items_s))[item];
+  if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
   int slice = 0;
   while (slice + 1 < a.n_slices && (int)blockIdx.y >= a.col_blk[slice + 1]) ++slice;
   const SliceRef &sl = a.sl[slice];
@@ -168,42 +270,21 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   const int wave = tid >> 6;
   const int kp = (r + 31) & ~31;  // ranks padded to the MFMA k step
 
-  // t = sum of the k-split partials, as bf16 hi + lo
-  for (int e = tid; e < RB * kp; e += 256) {
-    const int row = e / kp;
-    const int j = e - row * kp;
-    float v = 0.f;
-    if (row < nr && j < r) v = tpart_sum(tpart, it.pos + row, slice, j, a.ksplit, a.n_slices, a.R);
-    const uint16_t hi = f32_to_bf16_bits(v);
-    const uint16_t lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
-    th[row * KP + j] = hi;
-    tl[row * KP + j] = lo;
-  }
-  __syncthreads();
-
+  // 1. loads that do not depend on t, issued first: B fragments and the y
+  //    chunks this thread will update (row = chunk / 32, 8 columns each)
   const AdapterRef &ar = sl.ar;
   const int stride = ar.pooled ? r : ar.max_rank;  // B row stride (elements)
-  const bool vec_ok = (stride % 8) == 0;
-  f32x4_t acc[RBK][4];
+  const bool bvec = (stride % 8) == 0;
+  bf16x8_t fb[RMAX_MFMA / 32][4];
 #pragma unroll
-  for (int rb = 0; rb < RBK; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int jk = 0; jk < kp; jk += 32) {
-    const int jl = jk + (lane >> 4) * 8;
-    bf16x8_t fh[RBK], fl[RBK], fb[4];
-#pragma unroll
-    for (int rb = 0; rb < RBK; ++rb) {
-      fh[rb] = ld16(&th[(rb * 16 + (lane & 15)) * KP + jl]);
-      fl[rb] = ld16(&tl[(rb * 16 + (lane & 15)) * KP + jl]);
-    }
+  for (int ks = 0; ks < RMAX_MFMA / 32; ++ks) {
+    const int jl = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int64_t n = n0 + (wave * 4 + cb) * 16 + (lane & 15);
       bf16x8_t v = zero8();
-      if (n < sl.d && jl < r) {
-        if (vec_ok && jl + 8 <= r) {
+      if (ks * 32 < kp && n < sl.d && jl < r) {
+        if (bvec && jl + 8 <= r) {
           v = ld16(adapter_b_ptr(ar, it.adapter, r, n, jl));
         } else {
           uint16_t e8[8];
@@ -215,60 +296,130 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
           v = __builtin_bit_cast(bf16x8_t, e8);
         }
       }
-      fb[cb] = v;
+      fb[ks][cb] = v;
     }
+  }
+  const bool yvec = a.y_vec && (sl.col0 % 8) == 0;
+  uint16_t *yb = reinterpret_cast<uint16_t *>(a.y) + sl.col0;
+  uint16_t *yp[YCH];
+  uint4 yv[YCH];
 #pragma unroll
-    for (int rb = 0; rb < RBK; ++rb)
+  for (int c = 0; c < YCH; ++c) {
+    const int ch = tid + c * 256;
+    const int row = ch >> 5;
+    const int64_t n = n0 + (ch & 31) * 8;
+    yp[c] = nullptr;
+    yv[c] = make_uint4(0, 0, 0, 0);
+    if (row < nr && n < sl.d) {
+      yp[c] = yb + (int64_t)perm[it.pos + row] * a.ldy + n;
+      if (yvec && n + 8 <= sl.d) {
+        yv[c] = *reinterpret_cast<const uint4 *>(yp[c]);
+      } else {
+        uint16_t e8[8];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh[rb], fb[cb], acc[rb][cb], 0, 0, 0);
-        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[rb], fb[cb], acc[rb][cb], 0, 0, 0);
+        for (int q = 0; q < 8; ++q) e8[q] = (n + q < sl.d) ? yp[c][q] : (uint16_t)0;
+        yv[c] = __builtin_bit_cast(uint4, e8);
       }
+    }
   }
 
-  // y += scale * acc: every y value of this lane is loaded before any is
-  // stored (a store could alias a later load, so the compiler would
-  // otherwise serialise each read-modify-write on the load latency)
-  const float scale = sl.scales[it.adapter];
-  uint16_t *yb = reinterpret_cast<uint16_t *>(a.y) + sl.col0;
-  uint16_t *yp[RBK][4];
-  uint16_t yv[RBK][4][4];
-#pragma unroll
-  for (int rb = 0; rb < RBK; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rb * 16 + ((lane >> 4) << 2) + i;
-      yp[rb][i] = row < nr ? yb + (int64_t)perm[it.pos + row] * a.ldy : nullptr;
+  // 2. t = sum of the k-split partials, as bf16 hi + lo (4 ranks per thread)
+  const int kp4 = kp >> 2;
+  for (int e = tid; e < RB * kp4; e += 256) {
+    const int row = e / kp4;
+    const int j = (e - row * kp4) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < nr && j < r) {
+      v = tpart_sum4(tpart, it.pos + row, slice, j, a.ksplit, a.L.rows, a.n_slices, a.L.R);
+      // entries past the rank are never written by the shrink
+      if (j + 1 >= r) v.y = 0.f;
+      if (j + 2 >= r) v.z = 0.f;
+      if (j + 3 >= r) v.w = 0.f;
     }
+    const float f[4] = {v.x, v.y, v.z, v.w};
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      h[c] = f32_to_bf16_bits(f[c]);
+      l[c] = f32_to_bf16_bits(f[c] - bf16_bits_to_f32(h[c]));
+    }
+    *reinterpret_cast<uint2 *>(&th[row * KP + j]) =
+        make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+    *reinterpret_cast<uint2 *>(&tl[row * KP + j]) =
+        make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+  }
+  __syncthreads();
+
+  // 3. acc[rb][cb] = t (rows) x B_s^T (16 columns), on the matrix cores
+  f32x4_t acc[RBK][4];
 #pragma unroll
   for (int rb = 0; rb < RBK; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < RMAX_MFMA / 32; ++ks) {
+    if (ks * 32 >= kp) break;
+    const int jl = ks * 32 + (lane >> 4) * 8;
+#pragma unroll
+    for (int rb = 0; rb < RBK; ++rb) {
+      const bf16x8_t fh = ld16(&th[(rb * 16 + (lane & 15)) * KP + jl]);
+      const bf16x8_t fl = ld16(&tl[(rb * 16 + (lane & 15)) * KP + jl]);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const int64_t n = n0 + (wave * 4 + cb) * 16 + (lane & 15);
-        yv[rb][i][cb] = (yp[rb][i] != nullptr && n < sl.d) ? yp[rb][i][n] : (uint16_t)0;
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, fb[ks][cb], acc[rb][cb], 0, 0, 0);
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, fb[ks][cb], acc[rb][cb], 0, 0, 0);
       }
+    }
+  }
+
+  // 4. y += scale * acc, 16 rows at a time through LDS so that every thread
+  //    updates whole 16-byte runs of one y row (rounded once)
+  const float scale = sl.scales[it.adapter];
 #pragma unroll
-  for (int rb = 0; rb < RBK; ++rb)
+  for (int rb = 0; rb < RBK; ++rb) {
+    if (rb * 16 >= nr) break;  // uniform
+    if (rb > 0) __syncthreads();  // previous pass's reads of ys are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int64_t n = n0 + (wave * 4 + cb) * 16 + (lane & 15);
-        if (yp[rb][i] != nullptr && n < sl.d)
-          yp[rb][i][n] = f32_to_bf16_bits(bf16_bits_to_f32(yv[rb][i][cb]) + scale * acc[rb][cb][i]);
+      for (int i = 0; i < 4; ++i)
+        ys[(((lane >> 4) << 2) + i) * YLD + (wave * 4 + cb) * 16 + (lane & 15)] = acc[rb][cb][i];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = rb * 2 + h;
+      if (yp[c] == nullptr) continue;
+      const int ch = tid + h * 256;
+      const int lr = ch >> 5;  // row within the pass
+      const int col = (ch & 31) * 8;
+      const float4 s0 = *reinterpret_cast<const float4 *>(&ys[lr * YLD + col]);
+      const float4 s1 = *reinterpret_cast<const float4 *>(&ys[lr * YLD + col + 4]);
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      uint16_t e8[8];
+      const uint16_t *old = reinterpret_cast<const uint16_t *>(&yv[c]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) e8[q] = f32_to_bf16_bits(bf16_bits_to_f32(old[q]) + scale * sv[q]);
+      const int64_t n = n0 + col;
+      if (yvec && n + 8 <= sl.d) {
+        *reinterpret_cast<uint4 *>(yp[c]) = __builtin_bit_cast(uint4, e8);
+      } else {
+        for (int q = 0; q < 8; ++q)
+          if (n + q < sl.d) yp[c][q] = e8[q];
       }
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, hipStream_t st) {
+hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_slice,
+                              hipStream_t st) {
+  const unsigned gy = per_slice ? (unsigned)a.n_slices : 1u;
   if (rows_per_item == 16) {
-    dim3 grid((unsigned)a.L.items_g_cap, (unsigned)a.n_slices, (unsigned)a.ksplit);
+    dim3 grid((unsigned)a.L.items_g_cap, gy, (unsigned)a.ksplit);
     hipLaunchKernelGGL(k_shrink_mfma<16>, grid, dim3(256), 0, st, a);
   } else {
-    dim3 grid((unsigned)a.L.items_s_cap, (unsigned)a.n_slices, (unsigned)a.ksplit);
+    dim3 grid((unsigned)a.L.items_s_cap, gy, (unsigned)a.ksplit);
     hipLaunchKernelGGL(k_shrink_mfma<64>, grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();

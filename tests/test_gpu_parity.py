@@ -99,7 +99,8 @@ def _plan_case(oracle_mod, ids, S, ranks, R, pooled=None):
 
 
 @pytest.mark.parametrize("M,S,seed", [(0, 3, 0), (1, 3, 1), (64, 4, 2), (255, 7, 3), (512, 12, 4),
-                                      (2048, 1024, 5), (4097, 300, 6), (8192, 8, 7)])
+                                      (2048, 1024, 5), (4097, 300, 6), (8192, 8, 7),
+                                      (300, 5000, 9), (3000, 6000, 10)])
 def test_plan_random_ids(oracle_mod, M, S, seed):
     say("plan M=%d S=%d" % (M, S))
     rng = np.random.default_rng(seed)
@@ -121,6 +122,38 @@ def test_plan_structured(oracle_mod):
     ]:
         say("plan " + name)
         _plan_case(oracle_mod, ids, S, np.full(S, 8, np.int32), 16)
+
+
+@pytest.mark.parametrize("M,S,k,d,dtype", [(512, 12, 256, 288, torch.bfloat16),
+                                           (300, 8000, 64, 64, torch.bfloat16),
+                                           (200, 9, 64, 64, torch.float32),
+                                           (777, 40, 128, 96, torch.bfloat16)])
+def test_plan_inside_linear(oracle_mod, M, S, k, d, dtype):
+    # lora_linear computes the plan inside the base GEMM's launch (or just
+    # before it): the plan it leaves in the workspace is the oracle's
+    say("plan inside lora_linear M=%d S=%d k=%d d=%d %s" % (M, S, k, d, dtype))
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(M + S)
+    ids = rng.integers(-1, S, size=M).astype(np.int32)
+    ranks = rng.integers(0, 9, size=S).astype(np.int32)
+    R = 8
+    A = torch.zeros(S, R, k, dtype=dtype, device=dev)
+    B = torch.zeros(S, d, R, dtype=dtype, device=dev)
+    ranks_t = torch.from_numpy(ranks).to(dev)
+    ad = lr.Adapters.slots(A, B, ranks_t)
+    x = torch.randn(M, k, device=dev).to(dtype)
+    W = torch.randn(d, k, device=dev).to(dtype)
+    scales = torch.ones(S, dtype=torch.float32, device=dev)
+    ws = lr.new_workspace(M, d, k, dtype, ad, device=dev)
+    lr.lora_linear(x, W, ad, torch.from_numpy(ids).to(dev), scales, workspace=ws)
+    got = lr.lora_plan_view(ws, M, ad)
+    ref = oracle_mod.plan(ids, S, ranks, R)
+    assert got["n_adapted"] == ref["n_adapted"]
+    assert np.array_equal(got["perm"], ref["perm"])
+    assert np.array_equal(got["seg_adapter"], ref["seg_adapter"])
+    assert np.array_equal(got["seg_start"], ref["seg_start"])
+    assert np.array_equal(got["seg_len"], ref["seg_len"])
+    assert got["items_gather"] == sum((l + 15) // 16 for l in ref["seg_len"])
 
 
 def test_plan_pool_pages(oracle_mod):
