@@ -22,8 +22,9 @@
 //   LDS.  Output: fp32 partials, one per k split (summed in split order by
 //   the expand).
 // expand: y[perm[p], n] += scale_s * sum_j B_s[n, j] t[p, j]
-//   grid (item, 256-column block of any slice).  t (the sum of the k-split
-//   partials, in split order) is split into bf16 hi + lo parts (t = hi + lo to ~16 mantissa
+//   grid: (item, 256-column block of any slice), each column block kept on
+//   one XCD across items.  t (the sum of the k-split partials, in split
+//   order) is split into bf16 hi + lo parts (t = hi + lo to ~16 mantissa
 //   bits), so two MFMAs per block keep t's precision; B_s rows feed the B
 //   operand (ranks are contiguous in both slot and pool layouts).  Then
 //   y = y + scale * acc, rounded once.  Rows without an adapter are never
@@ -34,8 +35,8 @@ namespace lora {
 
 namespace {
 
-constexpr int ECB = 256;      // columns per expand workgroup
 constexpr int RMAX_MFMA = 64; // largest max_rank these kernels take
+constexpr int kExpandCols16 = 256;  // expand columns per workgroup, 16-row items (512 measured slower)
 
 __device__ __forceinline__ bf16x8_t ld16(const void *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
@@ -239,30 +240,43 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
   }
 }
 
-template <int RB>
+template <int RB, int ECB>
 __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   constexpr int RBK = RB / 16;
   constexpr int KP = RMAX_MFMA + 8;  // padded LDS row (bf16)
+  constexpr int CB = ECB / 64;       // 16-column blocks per wave
+  constexpr int CPR = ECB / 8;       // 16-byte y chunks per row
+  constexpr int CPT = 16 * CPR / 256;  // 16-byte y chunks per thread per 16-row pass
   constexpr int YLD = ECB + 4;       // transposed-output LDS row (fp32)
-  constexpr int YCH = 2 * RBK;       // 16-byte y chunks per thread
+  constexpr int YCH = CPT * RBK;     // 16-byte y chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t th[RB * KP];
   __shared__ __attribute__((aligned(16))) uint16_t tl[RB * KP];
   __shared__ __attribute__((aligned(16))) float ys[16 * YLD];
 
+  // Workgroup b runs on XCD b % 8.  A column block stays on one XCD for
+  // every item (cb = b % 8 + 8 * j), so the items of one adapter -- which
+  // read the same B rows -- share that XCD's L2 instead of each fetching
+  // B (whole 128-byte lines even for a small rank) from memory.
+  const int ncb = a.col_blk[a.n_slices];
+  const int per_xcd = (ncb + 7) >> 3;
+  const int b = blockIdx.x;
+  const int q = b >> 3;
+  const int item = q / per_xcd;
+  const int cbk = (b & 7) + 8 * (q - item * per_xcd);
+  if (cbk >= ncb) return;
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
-  const int item = blockIdx.x;
   // the item slot exists up to the list's capacity, so it is read beside
   // the count instead of after it
   const Item it =
       reinterpret_cast<const Item *>(a.ws + (RB == 16 ? a.L.items_g : a.L.items_s))[item];
   if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
   int slice = 0;
-  while (slice + 1 < a.n_slices && (int)blockIdx.y >= a.col_blk[slice + 1]) ++slice;
+  while (slice + 1 < a.n_slices && cbk >= a.col_blk[slice + 1]) ++slice;
   const SliceRef &sl = a.sl[slice];
   const int r = sl.ranks[it.adapter];
   if (r == 0) return;
   const int nr = it.nrows;
-  const int64_t n0 = (int64_t)(blockIdx.y - a.col_blk[slice]) * ECB;
+  const int64_t n0 = (int64_t)(cbk - a.col_blk[slice]) * ECB;
   const int32_t *perm = reinterpret_cast<const int32_t *>(a.ws + a.L.perm);
   const float *tpart = reinterpret_cast<const float *>(a.ws + a.L.tpart);
   const int tid = threadIdx.x;
@@ -271,21 +285,31 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   const int kp = (r + 31) & ~31;  // ranks padded to the MFMA k step
 
   // 1. loads that do not depend on t, issued first: B fragments and the y
-  //    chunks this thread will update (row = chunk / 32, 8 columns each)
+  //    chunks this thread will update (row = chunk / CPR, 8 columns each)
   const AdapterRef &ar = sl.ar;
   const int stride = ar.pooled ? r : ar.max_rank;  // B row stride (elements)
   const bool bvec = (stride % 8) == 0;
-  bf16x8_t fb[RMAX_MFMA / 32][4];
+  bf16x8_t fb[RMAX_MFMA / 32][CB];
 #pragma unroll
   for (int ks = 0; ks < RMAX_MFMA / 32; ++ks) {
     const int jl = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int64_t n = n0 + (wave * 4 + cb) * 16 + (lane & 15);
+    for (int cb = 0; cb < CB; ++cb) {
+      const int64_t n = n0 + (wave * CB + cb) * 16 + (lane & 15);
       bf16x8_t v = zero8();
       if (ks * 32 < kp && n < sl.d && jl < r) {
         if (bvec && jl + 8 <= r) {
           v = ld16(adapter_b_ptr(ar, it.adapter, r, n, jl));
+        } else if (bvec && !ar.pooled) {
+          // a slot row is padded to max_rank (a multiple of 8): load the
+          // whole 8-rank vector and zero the ranks past r (padding may hold
+          // anything)
+          uint16_t e8[8];
+          *reinterpret_cast<bf16x8_t *>(e8) = ld16(adapter_b_ptr(ar, it.adapter, r, n, jl));
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (jl + q >= r) e8[q] = 0;
+          v = __builtin_bit_cast(bf16x8_t, e8);
         } else {
           uint16_t e8[8];
 #pragma unroll
@@ -305,9 +329,9 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   uint4 yv[YCH];
 #pragma unroll
   for (int c = 0; c < YCH; ++c) {
-    const int ch = tid + c * 256;
-    const int row = ch >> 5;
-    const int64_t n = n0 + (ch & 31) * 8;
+    const int ch = (c / CPT) * 16 * CPR + tid + (c % CPT) * 256;  // pass c / CPT
+    const int row = ch / CPR;
+    const int64_t n = n0 + (ch % CPR) * 8;
     yp[c] = nullptr;
     yv[c] = make_uint4(0, 0, 0, 0);
     if (row < nr && n < sl.d) {
@@ -351,11 +375,11 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   __syncthreads();
 
   // 3. acc[rb][cb] = t (rows) x B_s^T (16 columns), on the matrix cores
-  f32x4_t acc[RBK][4];
+  f32x4_t acc[RBK][CB];
 #pragma unroll
   for (int rb = 0; rb < RBK; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < RMAX_MFMA / 32; ++ks) {
     if (ks * 32 >= kp) break;
@@ -365,7 +389,7 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
       const bf16x8_t fh = ld16(&th[(rb * 16 + (lane & 15)) * KP + jl]);
       const bf16x8_t fl = ld16(&tl[(rb * 16 + (lane & 15)) * KP + jl]);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, fb[ks][cb], acc[rb][cb], 0, 0, 0);
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, fb[ks][cb], acc[rb][cb], 0, 0, 0);
       }
@@ -380,18 +404,18 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
     if (rb * 16 >= nr) break;  // uniform
     if (rb > 0) __syncthreads();  // previous pass's reads of ys are done
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        ys[(((lane >> 4) << 2) + i) * YLD + (wave * 4 + cb) * 16 + (lane & 15)] = acc[rb][cb][i];
+        ys[(((lane >> 4) << 2) + i) * YLD + (wave * CB + cb) * 16 + (lane & 15)] = acc[rb][cb][i];
     __syncthreads();
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = rb * 2 + h;
+    for (int h = 0; h < CPT; ++h) {
+      const int c = rb * CPT + h;
       if (yp[c] == nullptr) continue;
       const int ch = tid + h * 256;
-      const int lr = ch >> 5;  // row within the pass
-      const int col = (ch & 31) * 8;
+      const int lr = ch / CPR;  // row within the pass
+      const int col = (ch % CPR) * 8;
       const float4 s0 = *reinterpret_cast<const float4 *>(&ys[lr * YLD + col]);
       const float4 s1 = *reinterpret_cast<const float4 *>(&ys[lr * YLD + col + 4]);
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -426,16 +450,19 @@ hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_sli
 }
 
 hipError_t launch_expand_sgmv(const LoraArgs &a0, int rows_per_item, hipStream_t st) {
+  const int ecb = rows_per_item == 16 ? kExpandCols16 : 256;
   LoraArgs a = a0;
   a.col_blk[0] = 0;
   for (int q = 0; q < a.n_slices; ++q)
-    a.col_blk[q + 1] = a.col_blk[q] + (int32_t)((a.sl[q].d + ECB - 1) / ECB);
+    a.col_blk[q + 1] = a.col_blk[q] + (int32_t)((a.sl[q].d + ecb - 1) / ecb);
+  // one dimension: item-major, column blocks padded to a multiple of 8
+  const int64_t cb8 = ((int64_t)a.col_blk[a.n_slices] + 7) / 8 * 8;
   if (rows_per_item == 16) {
-    dim3 grid((unsigned)a.L.items_g_cap, (unsigned)a.col_blk[a.n_slices]);
-    hipLaunchKernelGGL(k_expand_mfma<16>, grid, dim3(256), 0, st, a);
+    const dim3 grid((unsigned)(a.L.items_g_cap * cb8));
+    hipLaunchKernelGGL((k_expand_mfma<16, kExpandCols16>), grid, dim3(256), 0, st, a);
   } else {
-    dim3 grid((unsigned)a.L.items_s_cap, (unsigned)a.col_blk[a.n_slices]);
-    hipLaunchKernelGGL(k_expand_mfma<64>, grid, dim3(256), 0, st, a);
+    const dim3 grid((unsigned)(a.L.items_s_cap * cb8));
+    hipLaunchKernelGGL((k_expand_mfma<64, 256>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
