@@ -57,6 +57,14 @@ struct Item {
   int32_t seg;
 };
 
+// Beside each 16-row work item: the adapter's rank in every slice and the
+// item's rows (perm[pos .. pos + nrows)), so a kernel reads them together
+// with the item instead of one dependent load after another.
+struct ItemRows {
+  int32_t r[kMaxSlices];
+  int32_t rows[kRowsPerGatherItem];
+};
+
 // Where one adapter's A and B live.  SLOTS: A [S, R, k] and B [S, d, R];
 // POOL: logical space [A r x k | B d x r] cut into pages.
 struct AdapterRef {

@@ -17,7 +17,7 @@ struct WsLayout {
   int64_t items_s_cap = 0;
   int32_t R = 0;  // fp32 partial row width: max rank rounded up to 4
   size_t hdr = 0, perm = 0, seg_adapter = 0, seg_start = 0, seg_len = 0;
-  size_t items_g = 0, items_s = 0, tpart = 0, total = 0;
+  size_t items_g = 0, items_gx = 0, items_s = 0, tpart = 0, total = 0;
 };
 WsLayout ws_layout(int64_t rows, int32_t S, int32_t R, int32_t n_slices);
 

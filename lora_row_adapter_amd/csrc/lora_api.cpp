@@ -39,6 +39,7 @@ WsLayout ws_layout(int64_t rows, int32_t S, int32_t R, int32_t n_slices) {
   L.seg_start = take((size_t)L.seg_cap * sizeof(int32_t));
   L.seg_len = take((size_t)L.seg_cap * sizeof(int32_t));
   L.items_g = take((size_t)L.items_g_cap * sizeof(Item));
+  L.items_gx = take((size_t)L.items_g_cap * sizeof(ItemRows));
   L.items_s = take((size_t)L.items_s_cap * sizeof(Item));
   L.tpart = take((size_t)kMaxKSplit * L.rows * n_slices * L.R * sizeof(float));
   L.total = off;

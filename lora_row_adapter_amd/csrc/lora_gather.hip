@@ -81,19 +81,20 @@ __global__ __launch_bounds__(256) void k_shrink_gather(LoraArgs a) {
 
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
   const int item = blockIdx.x;
-  if (item >= hdr[kHdrItemsGather]) return;
+  // item slots exist up to the list's capacity: read them beside the count
   const Item it = reinterpret_cast<const Item *>(a.ws + a.L.items_g)[item];
+  const ItemRows *ix = reinterpret_cast<const ItemRows *>(a.ws + a.L.items_gx) + item;
+  if (item >= hdr[kHdrItemsGather]) return;
   const int jblocks = (a.R + JB - 1) / JB;
   const int slice = blockIdx.y / jblocks;
   const SliceRef &sl = a.sl[slice];
-  const int r = sl.ranks[it.adapter];
+  const int r = ix->r[slice];
   const int j0 = (blockIdx.y - slice * jblocks) * JB;
   if (j0 >= r) return;
   const int nj = min(JB, r - j0);
   const int64_t kbeg = (int64_t)blockIdx.z * a.kchunk;
   if (kbeg >= a.k) return;
   const int64_t kend = min(a.k, kbeg + a.kchunk);
-  const int32_t *perm = reinterpret_cast<const int32_t *>(a.ws + a.L.perm);
   float *tpart = reinterpret_cast<float *>(a.ws + a.L.tpart);
 
   const int tid = threadIdx.x;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void k_shrink_gather(LoraArgs a) {
   for (int rr = 0; rr < RPW; ++rr) {
     const int p = wave * RPW + rr;
     rowv[rr] = p < it.nrows;
-    rowoff[rr] = rowv[rr] ? (int64_t)perm[it.pos + p] * a.ldx : 0;
+    rowoff[rr] = rowv[rr] ? (int64_t)ix->rows[p] * a.ldx : 0;
   }
 
   float acc[64];
@@ -193,15 +194,15 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
 
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
   const int item = blockIdx.x;
-  if (item >= hdr[kHdrItemsGather]) return;
   const Item it = reinterpret_cast<const Item *>(a.ws + a.L.items_g)[item];
+  const ItemRows *ix = reinterpret_cast<const ItemRows *>(a.ws + a.L.items_gx) + item;
+  if (item >= hdr[kHdrItemsGather]) return;
   int slice = 0;
   while (slice + 1 < a.n_slices && (int)blockIdx.y >= a.col_blk[slice + 1]) ++slice;
   const SliceRef &sl = a.sl[slice];
-  const int r = sl.ranks[it.adapter];
+  const int r = ix->r[slice];
   if (r == 0) return;
   const int nr = it.nrows;
-  const int32_t *perm = reinterpret_cast<const int32_t *>(a.ws + a.L.perm);
   const float *tpart = reinterpret_cast<const float *>(a.ws + a.L.tpart);
   const int tid = threadIdx.x;
 
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(256) void k_expand_gather(LoraArgs a) {
   T y0[kRowsPerGatherItem], y1[kRowsPerGatherItem];
 #pragma unroll
   for (int row = 0; row < kRowsPerGatherItem; ++row) {
-    yr[row] = row < nr ? yb + (int64_t)perm[it.pos + row] * a.ldy + n : nullptr;
+    yr[row] = row < nr ? yb + (int64_t)ix->rows[row] * a.ldy + n : nullptr;
     y0[row] = yr[row] ? yr[row][0] : T(0);
     y1[row] = (yr[row] && c1) ? yr[row][1] : T(0);
   }

@@ -80,32 +80,66 @@ __device__ __forceinline__ const uint8_t *arow_ptr(const ARow &w, int64_t kk) {
 }
 
 // The item's rank blocks over all slices, in slice order: block v is
-// (slice, 16-rank block) with 16 * block < r_slice.  Returns the count and,
-// for v, its slice / block / rank.
-__device__ __forceinline__ int vblock_count(const LoraArgs &a, int adapter) {
+// (slice, 16-rank block) with 16 * block < r_slice.  rk: the adapter's rank
+// in every slice.  Returns the count and, for v, its slice / block / rank.
+__device__ __forceinline__ int vblock_count(const LoraArgs &a, const int (&rk)[kMaxSlices]) {
   int n = 0;
-  for (int q = 0; q < a.n_slices; ++q) n += (a.sl[q].ranks[adapter] + 15) >> 4;
+#pragma unroll
+  for (int q = 0; q < kMaxSlices; ++q)
+    if (q < a.n_slices) n += (rk[q] + 15) >> 4;
   return n;
 }
-__device__ __forceinline__ void vblock_find(const LoraArgs &a, int adapter, int v, int &slice,
-                                            int &jb, int &r) {
+__device__ __forceinline__ void vblock_find(const LoraArgs &a, const int (&rk)[kMaxSlices], int v,
+                                            int &slice, int &jb, int &r) {
   slice = 0;
   jb = v;
-  r = a.sl[0].ranks[adapter];
-  for (int q = 0; q + 1 < a.n_slices; ++q) {
+  r = rk[0];
+  bool found = false;
+#pragma unroll
+  for (int q = 0; q + 1 < kMaxSlices; ++q) {
+    if (found || q + 1 >= a.n_slices) continue;
     const int nb = (r + 15) >> 4;
-    if (jb < nb) break;
+    if (jb < nb) {
+      found = true;
+      continue;
+    }
     jb -= nb;
     slice = q + 1;
-    r = a.sl[q + 1].ranks[adapter];
+    r = rk[q + 1];
   }
+}
+
+// The adapter's rank in every slice: from the 16-row item's record
+// (FROM_ITEM), else from the slices' rank arrays.
+template <bool FROM_ITEM>
+__device__ __forceinline__ void item_ranks(const LoraArgs &a, const ItemRows *ix, int adapter,
+                                           int (&rk)[kMaxSlices]) {
+#pragma unroll
+  for (int q = 0; q < kMaxSlices; ++q) {
+    if constexpr (FROM_ITEM)
+      rk[q] = q < a.n_slices ? ix->r[q] : 0;
+    else
+      rk[q] = q < a.n_slices ? a.sl[q].ranks[adapter] : 0;
+  }
+}
+
+// Row of sorted position it.pos + row: from the 16-row item's record, else
+// from perm.
+template <bool FROM_ITEM>
+__device__ __forceinline__ int item_row(const ItemRows *ix, const int32_t *perm, const Item &it,
+                                        int row) {
+  if constexpr (FROM_ITEM)
+    return ix->rows[row];
+  else
+    return perm[it.pos + row];
 }
 
 // Rank blocks [v0, v0 + G) of one item over one k split: MFMA partial
 // blocks per wave (alternate 32-wide k steps), summed in wave order through
 // LDS, written as this split's fp32 partials.
 template <int RB, int G, int U>
-__device__ __forceinline__ void shrink_blocks(const LoraArgs &a, const Item &it, int v0, int nvb,
+__device__ __forceinline__ void shrink_blocks(const LoraArgs &a, const Item &it,
+                                              const int (&rk)[kMaxSlices], int v0, int nvb,
                                               int64_t kbeg, int64_t kend,
                                               const int64_t (&xoff)[RB / 16],
                                               const bool (&xv)[RB / 16],
@@ -125,7 +159,7 @@ __device__ __forceinline__ void shrink_blocks(const LoraArgs &a, const Item &it,
     arow[g] = ARow{nullptr, nullptr, 0, 0, 0};
     if (v0 + g < nvb) {
       int slice, jb, r;
-      vblock_find(a, it.adapter, v0 + g, slice, jb, r);
+      vblock_find(a, rk, v0 + g, slice, jb, r);
       const int j = jb * 16 + (lane & 15);
       jv[g] = j < r;
       arow[g] = make_arow(a.sl[slice].ar, it.adapter, jv[g] ? j : 0);
@@ -176,7 +210,7 @@ __device__ __forceinline__ void shrink_blocks(const LoraArgs &a, const Item &it,
     const int g = blk % G;
     if (v0 + g < nvb) {
       int slice, jb, r;
-      vblock_find(a, it.adapter, v0 + g, slice, jb, r);
+      vblock_find(a, rk, v0 + g, slice, jb, r);
       const f32x4_t sum = ((red[0][wave][lane] + red[1][wave][lane]) + red[2][wave][lane]) +
                           red[3][wave][lane];
       const int j = jb * 16 + (lane & 15);
@@ -204,14 +238,22 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
   // the item slot exists up to the list's capacity: read it beside the count
   const Item it =
       reinterpret_cast<const Item *>(a.ws + (RB == 16 ? a.L.items_g : a.L.items_s))[item];
+  const ItemRows *ix = reinterpret_cast<const ItemRows *>(a.ws + a.L.items_gx) + item;
   if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
+  int rk[kMaxSlices];
+  item_ranks<RB == 16>(a, ix, it.adapter, rk);
   // grid.y == 1: every slice's rank blocks (x rows read once for all);
   // grid.y == n_slices: slice blockIdx.y's blocks only (more workgroups)
-  int vlo = 0, vhi = vblock_count(a, it.adapter);
+  int vlo = 0, vhi = vblock_count(a, rk);
   if (gridDim.y > 1) {
     vlo = 0;
-    for (int q = 0; q < (int)blockIdx.y; ++q) vlo += (a.sl[q].ranks[it.adapter] + 15) >> 4;
-    vhi = vlo + ((a.sl[blockIdx.y].ranks[it.adapter] + 15) >> 4);
+    int nb = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) {
+      if (q < (int)blockIdx.y) vlo += (rk[q] + 15) >> 4;
+      if (q == (int)blockIdx.y) nb = (rk[q] + 15) >> 4;
+    }
+    vhi = vlo + nb;
   }
   if (vhi == vlo) return;
   const int64_t kbeg = (int64_t)blockIdx.z * a.kchunk;
@@ -226,17 +268,17 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
   for (int rb = 0; rb < RBK; ++rb) {
     const int row = rb * 16 + (lane & 15);
     xv[rb] = row < it.nrows;
-    xoff[rb] = xv[rb] ? (int64_t)perm[it.pos + row] * a.ldx : 0;
+    xoff[rb] = xv[rb] ? (int64_t)item_row<RB == 16>(ix, perm, it, row) * a.ldx : 0;
   }
 
   // block groups sized so that few blocks keep several k steps of loads
   // in flight; up to 8 blocks (two projections of rank 64) share one read
   // of the x rows, more take another pass over them
   if (vhi - vlo <= 4) {
-    shrink_blocks<RB, 4, 4>(a, it, vlo, vhi, kbeg, kend, xoff, xv, red);
+    shrink_blocks<RB, 4, 4>(a, it, rk, vlo, vhi, kbeg, kend, xoff, xv, red);
   } else {
     for (int v0 = vlo; v0 < vhi; v0 += 8)
-      shrink_blocks<RB, 8, RB == 16 ? 2 : 1>(a, it, v0, vhi, kbeg, kend, xoff, xv, red);
+      shrink_blocks<RB, 8, RB == 16 ? 2 : 1>(a, it, rk, v0, vhi, kbeg, kend, xoff, xv, red);
   }
 }
 
@@ -269,11 +311,16 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   // the count instead of after it
   const Item it =
       reinterpret_cast<const Item *>(a.ws + (RB == 16 ? a.L.items_g : a.L.items_s))[item];
+  const ItemRows *ix = reinterpret_cast<const ItemRows *>(a.ws + a.L.items_gx) + item;
   if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
   int slice = 0;
   while (slice + 1 < a.n_slices && cbk >= a.col_blk[slice + 1]) ++slice;
   const SliceRef &sl = a.sl[slice];
-  const int r = sl.ranks[it.adapter];
+  int r;
+  if constexpr (RB == 16)
+    r = ix->r[slice];
+  else
+    r = sl.ranks[it.adapter];
   if (r == 0) return;
   const int nr = it.nrows;
   const int64_t n0 = (int64_t)(cbk - a.col_blk[slice]) * ECB;
@@ -335,7 +382,7 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
     yp[c] = nullptr;
     yv[c] = make_uint4(0, 0, 0, 0);
     if (row < nr && n < sl.d) {
-      yp[c] = yb + (int64_t)perm[it.pos + row] * a.ldy + n;
+      yp[c] = yb + (int64_t)item_row<RB == 16>(ix, perm, it, row) * a.ldy + n;
       if (yvec && n + 8 <= sl.d) {
         yv[c] = *reinterpret_cast<const uint4 *>(yp[c]);
       } else {

@@ -116,6 +116,7 @@ __device__ __forceinline__ void plan_bitonic(const PlanArgs &a, uint8_t *plan_ld
   int32_t *seg_start = reinterpret_cast<int32_t *>(a.ws + a.L.seg_start);
   int32_t *seg_len = reinterpret_cast<int32_t *>(a.ws + a.L.seg_len);
   Item *items_g = reinterpret_cast<Item *>(a.ws + a.L.items_g);
+  ItemRows *items_gx = reinterpret_cast<ItemRows *>(a.ws + a.L.items_gx);
   Item *items_s = reinterpret_cast<Item *>(a.ws + a.L.items_s);
 
   if (tid < 4) cnt[tid] = 0;
@@ -192,12 +193,19 @@ __device__ __forceinline__ void plan_bitonic(const PlanArgs &a, uint8_t *plan_ld
     const int st = sstart[s];
     const int len = ((s + 1 < n_seg) ? (int)sstart[s + 1] : n_ad) - st;
     const int ad = (int)(keys[st] >> a.row_bits);
+    int rk[kMaxSlices];
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) rk[q] = q < a.n_slices ? a.sl[q].ranks[ad] : 0;
     for (int p = 0; p < len; p += kRowsPerGatherItem) {
       Item it;
       it.adapter = ad;
       it.pos = st + p;
       it.nrows = min(kRowsPerGatherItem, len - p);
       it.seg = s;
+      ItemRows &ix = items_gx[og];
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q) ix.r[q] = rk[q];
+      for (int q = 0; q < it.nrows; ++q) ix.rows[q] = (int32_t)(keys[st + p + q] & rmask);
       items_g[og++] = it;
     }
     for (int p = 0; p < len; p += kRowsPerSgmvItem) {
@@ -227,11 +235,13 @@ __device__ __forceinline__ void plan_bitonic(const PlanArgs &a, uint8_t *plan_ld
 __host__ __device__ constexpr size_t plan_align16(size_t v) { return (v + 15) & ~(size_t)15; }
 __host__ __device__ constexpr size_t plan_sort_lds(int row_bits) { return (size_t)6 << row_bits; }
 __host__ __device__ constexpr size_t plan_count_lds(int M, int S, int NT) {
-  return plan_align16((size_t)M * 4) + plan_align16((size_t)S * 4) * (1 + NT / 64);
+  return plan_align16((size_t)M * 4) + plan_align16((size_t)S * 4) * (2 + NT / 64);
 }
 
 // Counting-sort plan.  `lds` holds plan_count_lds(M, S, NT) bytes: the
-// rows' adapters [M], a histogram [S] and per-wave counts [NT / 64][S].
+// rows' adapters [M], a histogram [S] (then each adapter's first sorted
+// position), each adapter's first gather item [S] and per-wave counts
+// [NT / 64][S].
 // Wave w owns the rows [w * RPW, (w + 1) * RPW): the per-wave counts give
 // each (wave, adapter) its first sorted position, and the wave then places
 // its rows in row order, so equal adapters keep row order (stable).
@@ -248,13 +258,15 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
   const int S = a.S;
   int *binv = reinterpret_cast<int *>(lds);
   int *hist = reinterpret_cast<int *>(lds + plan_align16((size_t)M * 4));
-  int *cntw = hist + plan_align16((size_t)S * 4) / 4;
+  int *ibase = hist + plan_align16((size_t)S * 4) / 4;
+  int *cntw = ibase + plan_align16((size_t)S * 4) / 4;
   int32_t *hdr = reinterpret_cast<int32_t *>(a.ws + a.L.hdr);
   int32_t *perm = reinterpret_cast<int32_t *>(a.ws + a.L.perm);
   int32_t *seg_adapter = reinterpret_cast<int32_t *>(a.ws + a.L.seg_adapter);
   int32_t *seg_start = reinterpret_cast<int32_t *>(a.ws + a.L.seg_start);
   int32_t *seg_len = reinterpret_cast<int32_t *>(a.ws + a.L.seg_len);
   Item *items_g = reinterpret_cast<Item *>(a.ws + a.L.items_g);
+  ItemRows *items_gx = reinterpret_cast<ItemRows *>(a.ws + a.L.items_gx);
   Item *items_s = reinterpret_cast<Item *>(a.ws + a.L.items_s);
   const int RPW = ((M + NW - 1) / NW + 63) & ~63;  // rows per wave, whole 64-row chunks
 
@@ -293,16 +305,23 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
   int os = block_exclusive_scan<NT>(ns, wsum, &n_items_s);
   for (int s = s0; s < s1; ++s) {
     const int h = hist[s];
+    hist[s] = orow;  // from here on: the adapter's first sorted position
+    ibase[s] = og;
     if (h > 0) {
       seg_adapter[oseg] = s;
       seg_start[oseg] = orow;
       seg_len[oseg] = h;
+      int rk[kMaxSlices];
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q) rk[q] = q < a.n_slices ? a.sl[q].ranks[s] : 0;
       for (int p = 0; p < h; p += kRowsPerGatherItem) {
         Item it;
         it.adapter = s;
         it.pos = orow + p;
         it.nrows = min(kRowsPerGatherItem, h - p);
         it.seg = oseg;
+#pragma unroll
+        for (int q = 0; q < kMaxSlices; ++q) items_gx[og].r[q] = rk[q];
         items_g[og++] = it;
       }
       for (int p = 0; p < h; p += kRowsPerSgmvItem) {
@@ -338,7 +357,12 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
       const int lb = __shfl(b, leader, 64);
       const uint64_t mask = __ballot(b == lb);
       const int first = cntw[wave * S + lb];
-      if (b == lb) perm[first + __popcll(mask & ((1ull << lane) - 1ull))] = m;
+      if (b == lb) {
+        const int pos = first + __popcll(mask & ((1ull << lane) - 1ull));
+        perm[pos] = m;
+        const int rel = pos - hist[lb];
+        items_gx[ibase[lb] + rel / kRowsPerGatherItem].rows[rel % kRowsPerGatherItem] = m;
+      }
       if (lane == leader) cntw[wave * S + lb] = first + __popcll(mask);
       pending &= ~mask;
     }
