@@ -18,6 +18,8 @@ Prints one JSON line (rank 0):
   roofline   = base GEMM (the dominant kernel) MFMA TFLOP/s vs the bf16 peak,
                from per-launch HIP events recorded on the launch stream
   cpu_baseline = the fp64 oracle on a bounded row sample, on the host cores
+  adapter_activation = host-to-device loading of the same adapters through
+               the pool manager (GB/s against the PCIe 5.0 x16 link)
 """
 import argparse
 import hashlib
@@ -55,6 +57,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-activation", action="store_true",
+                    help="skip the adapter-activation (host-to-device) measurement")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/ summaries from a rocprofv3 run whose trace/, fetch/, "
                          "write/, cfetch/, cwrite/ output directories are under DIR, and exit")
@@ -238,9 +242,80 @@ def main():
         },
     }
 
+    if not args.no_activation:
+        result["adapter_activation"] = adapter_activation(lr, w, pq, pv, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, pq, pv, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def adapter_activation(lr, w, pq, pv, stream, page_bytes=65536, reps=20):
+    """Host-to-device activation of the workload's 12 adapters (q and v
+    weights) into two managed pools of 64 KiB pages, from pinned host memory.
+
+    warm: one batch per pool, every adapter reloaded in place (rows kernel +
+          copy kernel);
+    cold: every adapter evicted, then one batch per pool (placement too);
+    single_calls: warm, but one lora_pool_load call per adapter;
+    copy: one plain pinned-to-device copy of the same number of bytes."""
+    pools, host = [], []
+    total = 0
+    for p in (pq, pv):
+        pages = [-(-int(r) * (w.k + p.d) * 2 // page_bytes) for r in w.ranks]
+        pools.append(lr.AdapterPool(sum(pages), page_bytes, w.S, max(pages), w.max_rank, w.k, p.d,
+                                    dtype=torch.bfloat16, device="cuda", stream=stream))
+        host.append([(p.A[s].pin_memory(), p.B[s].pin_memory()) for s in range(w.S)])
+        total += sum(int(r) * (w.k + p.d) * 2 for r in w.ranks)
+
+    def load_all(evict_first, batch=True):
+        for pool, hs in zip(pools, host):
+            if evict_first:
+                for s in range(w.S):
+                    pool.evict(s, stream=stream)
+            if batch:
+                pool.load_batch([(s, A, B) for s, (A, B) in enumerate(hs)], stream=stream)
+            else:
+                for s, (A, B) in enumerate(hs):
+                    pool.load(s, A, B, stream=stream)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        host_us = (time.perf_counter() - t0) * 1e6 / reps
+        return e0.elapsed_time(e1) * 1e3 / reps, host_us
+
+    warm_us, warm_host = timed(lambda: load_all(False))
+    cold_us, cold_host = timed(lambda: load_all(True))
+    single_us, single_host = timed(lambda: load_all(False, batch=False))
+    src = torch.empty(total, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(total, dtype=torch.uint8, device="cuda")
+    copy_us, _ = timed(lambda: dst.copy_(src, non_blocking=True))
+    st = [pl.stats() for pl in pools]
+    peak = 64.0  # PCIe 5.0 x16, one direction
+    res = {
+        "what": "H2D activation of the 12 q+v adapters (%.2f MB) into managed 64 KiB-page pools, "
+                "pinned host source, %d reps" % (total / 1e6, reps),
+        "bytes": total,
+        "warm_us": round(warm_us, 2), "warm_gbs": round(total / warm_us / 1e3, 2),
+        "cold_us": round(cold_us, 2), "cold_gbs": round(total / cold_us / 1e3, 2),
+        "single_calls_us": round(single_us, 2),
+        "single_calls_gbs": round(total / single_us / 1e3, 2),
+        "plain_copy_us": round(copy_us, 2), "plain_copy_gbs": round(total / copy_us / 1e3, 2),
+        "host_us_per_set": {"warm": round(warm_host, 1), "cold": round(cold_host, 1),
+                            "single_calls": round(single_host, 1)},
+        "link_peak_gbs": peak, "frac_link_warm": round(total / warm_us / 1e3 / peak, 4),
+        "frac_of_plain_copy_warm": round(copy_us / warm_us, 4),
+        "evictions": sum(x["evictions"] for x in st),
+    }
+    log("adapter activation: " + json.dumps(res))
+    return res
 
 
 def cpu_baseline(w, pq, pv, target_s):

@@ -75,6 +75,32 @@ class _CProfile(ctypes.Structure):
     ]
 
 
+class _CPoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("pool", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("ranks", ctypes.c_void_p),
+        ("n_pages", ctypes.c_int64),
+        ("page_bytes", ctypes.c_int64),
+        ("n_adapters", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("max_rank", ctypes.c_int32),
+        ("elem_bytes", ctypes.c_int32),
+        ("k", ctypes.c_int64),
+        ("d", ctypes.c_int64),
+    ]
+
+
+class _CPoolStats(ctypes.Structure):
+    _fields_ = [
+        ("loads", ctypes.c_int64),
+        ("evictions", ctypes.c_int64),
+        ("bytes_copied", ctypes.c_int64),
+        ("free_pages", ctypes.c_int64),
+        ("resident", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -123,6 +149,26 @@ def load_library():
     lib.lora_profile_enable.restype = i32
     lib.lora_profile_read.argtypes = [ctypes.POINTER(_CProfile), i32]
     lib.lora_profile_read.restype = i32
+    pi32 = ctypes.POINTER(i32)
+    lib.lora_pool_create.argtypes = [ctypes.POINTER(_CPoolDesc), p, ctypes.POINTER(p)]
+    lib.lora_pool_create.restype = i32
+    lib.lora_pool_destroy.argtypes = [p]
+    lib.lora_pool_destroy.restype = None
+    lib.lora_pool_adapters.argtypes = [p, pad]
+    lib.lora_pool_adapters.restype = i32
+    lib.lora_pool_load.argtypes = [p, i32, i32, p, p, p]
+    lib.lora_pool_load.restype = i32
+    lib.lora_pool_load_batch.argtypes = [p, i32, pi32, pi32, ctypes.POINTER(p), ctypes.POINTER(p), p]
+    lib.lora_pool_load_batch.restype = i32
+    lib.lora_pool_evict.argtypes = [p, i32, p]
+    lib.lora_pool_evict.restype = i32
+    for name in ("lora_pool_touch", "lora_pool_pin", "lora_pool_unpin"):
+        getattr(lib, name).argtypes = [p, pi32, i32]
+        getattr(lib, name).restype = i32
+    lib.lora_pool_query.argtypes = [p, i32, pi32, pi32, pi32, pi32, pi32]
+    lib.lora_pool_query.restype = i32
+    lib.lora_pool_get_stats.argtypes = [p, ctypes.POINTER(_CPoolStats)]
+    lib.lora_pool_get_stats.restype = i32
     _lib = lib
     return lib
 
@@ -231,6 +277,152 @@ class Adapters:
 
     def ref(self):
         return ctypes.byref(self._c)
+
+
+class AdapterPool:
+    """Adapter activation into a paged device pool (include/lora_pool.h).
+
+    With ``device`` set, the pool bytes, page table and ranks are allocated
+    here as torch tensors and handed to the manager; ``adapters()`` is the
+    POOL adapter set lora_linear reads.  With ``device=None`` the manager
+    runs in accounting-only mode (placement, LRU and pinning decisions with
+    no device memory)."""
+
+    def __init__(self, n_pages: int, page_bytes: int, n_adapters: int, max_pages: int,
+                 max_rank: int, k: int, d: int, dtype: torch.dtype = torch.bfloat16,
+                 device=None, stream=None):
+        lib = load_library()
+        self.dtype = dtype
+        self.k, self.d = int(k), int(d)
+        self.max_pages = int(max_pages)
+        self.page_bytes = int(page_bytes)
+        c = _CPoolDesc()
+        c.n_pages, c.page_bytes = int(n_pages), self.page_bytes
+        c.n_adapters, c.max_pages, c.max_rank = int(n_adapters), self.max_pages, int(max_rank)
+        c.elem_bytes = torch.empty((), dtype=dtype).element_size()
+        c.k, c.d = self.k, self.d
+        self.pool = self.page_table = self.ranks = None
+        if device is not None:
+            self.pool = torch.empty(int(n_pages) * self.page_bytes, dtype=torch.uint8, device=device)
+            self.page_table = torch.empty((int(n_adapters), self.max_pages), dtype=torch.int32,
+                                          device=device)
+            self.ranks = torch.empty(int(n_adapters), dtype=torch.int32, device=device)
+            c.pool = self.pool.data_ptr()
+            c.page_table = self.page_table.data_ptr()
+            c.ranks = self.ranks.data_ptr()
+        self._desc = c
+        self._inflight = []  # (event, host A, host B) of pinned loads not yet reached
+        h = ctypes.c_void_p()
+        st = _stream_ptr(stream) if device is not None else 0
+        _check(lib.lora_pool_create(ctypes.byref(c), st, ctypes.byref(h)), "lora_pool_create")
+        self._h = h
+
+    def __del__(self):
+        for ev, _ in getattr(self, "_inflight", []):
+            try:
+                ev.synchronize()
+            except Exception:  # pragma: no cover - interpreter shutdown
+                pass
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.lora_pool_destroy(h)
+            self._h = None
+
+    def _stream(self, stream) -> int:
+        return _stream_ptr(stream) if self.pool is not None else 0
+
+    def adapters(self) -> Adapters:
+        """The POOL adapter set over this manager's device tensors."""
+        if self.pool is None:
+            raise ValueError("an accounting-only pool has no device adapter set")
+        return Adapters.paged(self.pool, self.page_table, self.ranks, self.page_bytes,
+                              self._desc.max_rank)
+
+    def _weights(self, A, B, rank):
+        """(rank, A pointer, B pointer) after checking the host tensors."""
+        if A is None:
+            if rank is None:
+                raise ValueError("rank is needed when no weights are given")
+            return int(rank), 0, 0
+        if A.is_cuda or B.is_cuda:
+            raise ValueError("A and B are host tensors")
+        if A.dtype != self.dtype or B.dtype != self.dtype:
+            raise TypeError("A and B must be %s" % self.dtype)
+        if A.dim() != 2 or B.dim() != 2 or A.shape[1] != self.k or B.shape[0] != self.d \
+                or B.shape[1] != A.shape[0]:
+            raise ValueError("A must be [r, %d] and B [%d, r]" % (self.k, self.d))
+        if not (A.is_contiguous() and B.is_contiguous()):
+            raise ValueError("A and B must be contiguous")
+        return int(A.shape[0] if rank is None else rank), A.data_ptr(), B.data_ptr()
+
+    def _keep_alive(self, tensors, stream):
+        # Pinned sources are read by the device after the call returns: keep
+        # the tensors alive until the stream has passed the copy (torch's
+        # pinned-memory cache would otherwise hand the block to the next
+        # pin_memory() call).
+        pinned = [t for t in tensors if t is not None and t.is_pinned()]
+        if pinned and self.pool is not None:
+            ev = torch.cuda.Event()
+            ev.record(stream if stream is not None else torch.cuda.current_stream())
+            self._inflight.append((ev, pinned))
+
+    def load(self, adapter: int, A: Optional[torch.Tensor], B: Optional[torch.Tensor],
+             rank: Optional[int] = None, stream=None) -> None:
+        """Make ``adapter`` resident: A [r, k] and B [d, r], host tensors in
+        the pool's dtype (pinned ones are read by the device asynchronously)."""
+        r, pa, pb = self._weights(A, B, rank)
+        self._inflight = [e for e in self._inflight if not e[0].query()]
+        _check(_lib.lora_pool_load(self._h, int(adapter), r, pa, pb, self._stream(stream)),
+               "lora_pool_load")
+        self._keep_alive([A, B], stream)
+
+    def load_batch(self, items, stream=None) -> None:
+        """Several loads in one call (all or nothing).  items: (adapter, A, B)
+        or (adapter, None, None, rank) tuples."""
+        n = len(items)
+        ids = (ctypes.c_int32 * n)()
+        ranks = (ctypes.c_int32 * n)()
+        pa = (ctypes.c_void_p * n)()
+        pb = (ctypes.c_void_p * n)()
+        keep = []
+        for i, it in enumerate(items):
+            A, B = it[1], it[2]
+            r, a_ptr, b_ptr = self._weights(A, B, it[3] if len(it) > 3 else None)
+            ids[i], ranks[i], pa[i], pb[i] = int(it[0]), r, a_ptr, b_ptr
+            keep += [A, B]
+        self._inflight = [e for e in self._inflight if not e[0].query()]
+        _check(_lib.lora_pool_load_batch(self._h, n, ids, ranks, pa, pb, self._stream(stream)),
+               "lora_pool_load_batch")
+        self._keep_alive(keep, stream)
+
+    def evict(self, adapter: int, stream=None) -> None:
+        _check(_lib.lora_pool_evict(self._h, int(adapter), self._stream(stream)), "lora_pool_evict")
+
+    def _ids(self, fn, ids, what):
+        arr = (ctypes.c_int32 * len(ids))(*[int(i) for i in ids])
+        _check(fn(self._h, arr, len(ids)), what)
+
+    def touch(self, ids) -> None:
+        self._ids(_lib.lora_pool_touch, ids, "lora_pool_touch")
+
+    def pin(self, ids) -> None:
+        self._ids(_lib.lora_pool_pin, ids, "lora_pool_pin")
+
+    def unpin(self, ids) -> None:
+        self._ids(_lib.lora_pool_unpin, ids, "lora_pool_unpin")
+
+    def query(self, adapter: int) -> dict:
+        res, rank, pins, npg = (ctypes.c_int32() for _ in range(4))
+        pages = (ctypes.c_int32 * self.max_pages)()
+        _check(_lib.lora_pool_query(self._h, int(adapter), ctypes.byref(res), ctypes.byref(rank),
+                                    ctypes.byref(pins), ctypes.byref(npg), pages), "lora_pool_query")
+        return {"resident": bool(res.value), "rank": rank.value, "pins": pins.value,
+                "n_pages": npg.value, "pages": list(pages)[:npg.value]}
+
+    def stats(self) -> dict:
+        st = _CPoolStats()
+        _check(_lib.lora_pool_get_stats(self._h, ctypes.byref(st)), "lora_pool_get_stats")
+        return {name: getattr(st, name) for name, _ in _CPoolStats._fields_}
 
 
 class Slice:

@@ -77,4 +77,47 @@ hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_sli
 hipError_t launch_expand_sgmv(const LoraArgs &a, int rows_per_item, hipStream_t st);
 constexpr int kMaxRankMfma = 64;
 
+// Adapter pool manager.  Kernel arguments carry the page lists and the
+// copy descriptors (each struct stays under 4 KiB).
+constexpr int kPoolRowsMax = 32;     // rows per k_pool_rows launch
+constexpr int kPoolRowVals = 768;    // page entries per k_pool_rows launch
+struct PoolRow {    // columns [j0, j0 + n_vals) of one row, from v[v0 ...]
+  int32_t adapter;
+  int32_t rank;      // -1: evicted
+  int32_t n_vals;
+  int32_t v0;
+  int32_t j0;
+  int32_t last;      // last piece of the row: columns after it get -1, the rank is written
+};
+struct PoolRowsArgs {
+  int32_t *page_table;
+  int32_t *ranks;
+  int32_t max_pages;
+  int32_t n_rows;
+  PoolRow row[kPoolRowsMax];
+  int32_t v[kPoolRowVals];
+};
+constexpr int kPoolPullMax = 64;  // adapters per k_pool_pull launch
+struct PoolPullDesc {
+  const uint8_t *a;  // device-visible address of host A (rank x k)
+  const uint8_t *b;  // device-visible address of host B (d x rank)
+  int64_t a_bytes;
+  int64_t total;     // a_bytes + b_bytes
+  int32_t adapter;
+  int32_t chunk0;    // first chunk (workgroup) of this adapter
+};
+struct PoolPullArgs {
+  uint8_t *pool;
+  const int32_t *page_table;
+  int32_t max_pages;
+  int32_t log2_page;
+  int32_t log2_chunk;  // <= log2_page
+  int32_t n_desc;
+  int32_t n_chunks;
+  PoolPullDesc d[kPoolPullMax];
+};
+hipError_t launch_pool_fill(int32_t *p, int64_t n, int32_t v, hipStream_t st);
+hipError_t launch_pool_rows(const PoolRowsArgs &a, hipStream_t st);
+hipError_t launch_pool_pull(const PoolPullArgs &a, hipStream_t st);
+
 }  // namespace lora

@@ -2,6 +2,7 @@
 header declares, and rejects bad arguments on the host before launching
 anything (no compute calls here)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -11,11 +12,11 @@ import lora_row_adapter_amd as lr
 from lora_row_adapter_amd import _binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lora_row.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^[A-Za-z_][\w \t\*]*?\b(lora_\w+)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if not n.endswith("_t")))
@@ -25,7 +26,10 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("lora_linear", "lora_gemm", "lora_plan", "lora_plan_view", "lora_translate",
                      "lora_check", "lora_workspace_bytes", "lora_abi_version", "lora_status_str",
-                     "lora_profile_enable", "lora_profile_read"):
+                     "lora_profile_enable", "lora_profile_read", "lora_pool_create",
+                     "lora_pool_load", "lora_pool_evict", "lora_pool_pin", "lora_pool_unpin",
+                     "lora_pool_touch", "lora_pool_query", "lora_pool_get_stats",
+                     "lora_pool_adapters", "lora_pool_destroy"):
         assert required in names
 
 
