@@ -20,6 +20,7 @@ Prints one JSON line (rank 0):
   cpu_baseline = the fp64 oracle on a bounded row sample, on the host cores
   adapter_activation = host-to-device loading of the same adapters through
                the pool manager (GB/s against the PCIe 5.0 x16 link)
+  merge      = lora_merge (W' = W + s B A) at the q and v shapes, HBM GB/s
 """
 import argparse
 import hashlib
@@ -59,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-activation", action="store_true",
                     help="skip the adapter-activation (host-to-device) measurement")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="skip the merged-weight (lora_merge) measurement")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/ summaries from a rocprofv3 run whose trace/, fetch/, "
                          "write/, cfetch/, cwrite/ output directories are under DIR, and exit")
@@ -244,9 +247,47 @@ def main():
 
     if not args.no_activation:
         result["adapter_activation"] = adapter_activation(lr, w, pq, pv, stream)
+    if not args.no_merge:
+        result["merge"] = merge_rate(lr, w, pq, pv, sets, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, pq, pv, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def merge_rate(lr, w, pq, pv, sets, stream, reps=20):
+    """lora_merge at the 70B shapes: W' = W + s B A for the q (8192 x 8192)
+    and v (1024 x 8192) weights, adapters of rank 16 and 64, out of place,
+    rotating over the buffer sets' weights; HBM bytes per launch = read W +
+    write W' + A and B once."""
+    out = {}
+    Wq_all = [s_["W"][:pq.d] for s_ in sets]
+    Wv_all = [s_["W"][pq.d:] for s_ in sets]
+    for name, p, Ws, sl in (("q", pq, Wq_all, 0), ("v", pv, Wv_all, 1)):
+        dsts = [torch.empty_like(Ws[0]) for _ in range(2)]
+        for a in (3, 9):  # ranks 16 and 64
+            r = int(w.ranks[a])
+
+            def go(i):
+                s_ = sets[i % len(sets)]
+                lr.lora_merge(Ws[i % len(Ws)], s_["slices"][sl].adapters, a,
+                              s_["slices"][sl].scales, out=dsts[i % 2], stream=stream)
+            for i in range(4):
+                go(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                go(i)
+            e1.record(stream)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            nbytes = (2 * p.d * w.k + r * (w.k + p.d)) * 2
+            gbs = nbytes / us / 1e3
+            out["%s_r%d" % (name, r)] = {"us": round(us, 2), "gbs": round(gbs, 1),
+                                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                         "bytes": nbytes}
+    log("merge: " + json.dumps(out))
+    return out
 
 
 def adapter_activation(lr, w, pq, pv, stream, page_bytes=65536, reps=20):

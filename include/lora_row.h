@@ -234,6 +234,27 @@ lora_status_t lora_plan_view(const void *workspace, size_t workspace_bytes, int6
                              const lora_adapters_t *adapters, lora_plan_view_t *out);
 
 /*
+ * Merged weight of one adapter, for the single-adapter fast path:
+ *   W_out = W + coef * scales[adapter] * B_a A_a        (W, W_out: [d, k])
+ * "Your LoRA Adapters Are Thrashing Your GPUs", section 02 (weight merging vs
+ * keeping adapters separate): with W' = W + (alpha/r) B A the layer is the
+ * plain x W'^T, one adapter at a time; coef = 1 merges, coef = -1 takes a
+ * merged adapter back out (up to the rounding of the two stores).  When
+ * every row of a batch uses the same adapter, lora_gemm with the merged
+ * weight replaces lora_linear.
+ *   adapters: SLOTS or POOL set (the adapter's rank is read on the device);
+ *   scales: device fp32 [n_adapters]; W, W_out: device, ldw / ldo >= k;
+ *   W_out == W (same ldw) merges in place; other overlaps are LORA_ERR_ARG.
+ * bf16: k, ldw, ldo multiples of 8, MFMA kernel, fp32 sum of the rank-r
+ * product, one RNE rounding of W + coef*s*BA; fp32: multiples of 4, VALU.
+ * A rank outside [0, max_rank] or missing pool pages (device-side errors)
+ * leave W_out = W.  Asynchronous on `stream`.
+ */
+lora_status_t lora_merge(lora_dtype_t dtype, int64_t d, int64_t k, const void *W, int64_t ldw,
+                         const lora_adapters_t *adapters, int32_t adapter, const float *scales,
+                         float coef, void *W_out, int64_t ldo, void *stream);
+
+/*
  * Page-table translation as the kernels do it, exported for bit-exact checks:
  * phys_off[i] = page_table[adapter[i]][logical_off[i] / page_bytes] * page_bytes
  *               + logical_off[i] % page_bytes,

@@ -141,6 +141,8 @@ def load_library():
     lib.lora_plan.restype = i32
     lib.lora_plan_view.argtypes = [p, sz, i64, pad, ctypes.POINTER(_CPlanView)]
     lib.lora_plan_view.restype = i32
+    lib.lora_merge.argtypes = [i32, i64, i64, p, i64, pad, i32, p, ctypes.c_float, p, i64, p]
+    lib.lora_merge.restype = i32
     lib.lora_translate.argtypes = [pad, p, p, i64, p, p]
     lib.lora_translate.restype = i32
     lib.lora_check.argtypes = [p, p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -578,6 +580,24 @@ def lora_plan_view(workspace: torch.Tensor, M: int, adapters: Adapters) -> dict:
         "perm": arr(v.perm, n_ad), "seg_adapter": arr(v.seg_adapter, n_seg),
         "seg_start": arr(v.seg_start, n_seg), "seg_len": arr(v.seg_len, n_seg),
     }
+
+
+def lora_merge(W: torch.Tensor, adapters: Adapters, adapter: int, scales: torch.Tensor,
+               coef: float = 1.0, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """W' = W + coef * scales[adapter] * B_a A_a (out=W merges in place)."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(W)
+    wp, ldw = _rows(W, "W")
+    op, ldo = _rows(out, "out")
+    if out.dtype != W.dtype or out.shape != W.shape:
+        raise TypeError("out must match W in dtype and shape")
+    if adapters.kind == KIND_SLOTS and adapters.A.dtype != W.dtype:
+        raise TypeError("adapter slots must have W's dtype")
+    _check(lib.lora_merge(_dtype_code(W), W.shape[0], W.shape[1], wp, ldw, adapters.ref(),
+                          int(adapter), _dev(scales, "scales", torch.float32), float(coef), op, ldo,
+                          _stream_ptr(stream)), "lora_merge")
+    return out
 
 
 def lora_translate(adapters: Adapters, adapter: torch.Tensor, logical_off: torch.Tensor,

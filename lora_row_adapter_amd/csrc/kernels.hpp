@@ -116,6 +116,24 @@ struct PoolPullArgs {
   int32_t n_chunks;
   PoolPullDesc d[kPoolPullMax];
 };
+// Merged weight of one adapter: Wo = W + coef * scales[adapter] * B A.
+struct MergeArgs {
+  int32_t dtype;  // 0 f32, 1 bf16
+  int64_t d, k;
+  const uint8_t *W;
+  int64_t ldw;    // elements
+  uint8_t *Wo;
+  int64_t ldo;
+  AdapterRef ar;
+  const int32_t *ranks;
+  const float *scales;
+  int32_t adapter;
+  float coef;
+  int32_t rp;      // bf16 LDS rank capacity: max_rank rounded up to 32
+  int64_t n_pages; // pool: pages in the pool
+};
+hipError_t launch_merge(const MergeArgs &m, hipStream_t st);
+
 hipError_t launch_pool_fill(int32_t *p, int64_t n, int32_t v, hipStream_t st);
 hipError_t launch_pool_rows(const PoolRowsArgs &a, hipStream_t st);
 hipError_t launch_pool_pull(const PoolPullArgs &a, hipStream_t st);

@@ -524,6 +524,42 @@ lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, c
                             workspace_bytes, path, flags, stream);
 }
 
+lora_status_t lora_merge(lora_dtype_t dtype, int64_t d, int64_t k, const void *W, int64_t ldw,
+                         const lora_adapters_t *adapters, int32_t adapter, const float *scales,
+                         float coef, void *W_out, int64_t ldo, void *stream) {
+  if (dtype != LORA_DTYPE_F32 && dtype != LORA_DTYPE_BF16) return LORA_ERR_DTYPE;
+  if (d < 1 || k < 1 || d > INT32_MAX || k > INT32_MAX) return LORA_ERR_SHAPE;
+  if (W == nullptr || W_out == nullptr || scales == nullptr) return LORA_ERR_ARG;
+  lora_status_t s = check_adapters(adapters, 1);
+  if (s != LORA_OK) return s;
+  if (adapter < 0 || adapter >= adapters->n_adapters) return LORA_ERR_ARG;
+  if (ldw < k || ldo < k) return LORA_ERR_SHAPE;
+  const int64_t vec = dtype == LORA_DTYPE_BF16 ? 8 : 4;
+  if (k % vec || ldw % vec || ldo % vec || !aligned16(W) || !aligned16(W_out)) return LORA_ERR_SHAPE;
+  // in place is allowed; any other overlap is not
+  const int64_t eb = dtype == LORA_DTYPE_BF16 ? 2 : 4;
+  const uint8_t *wb = (const uint8_t *)W, *ob = (const uint8_t *)W_out;
+  const int64_t wspan = ((d - 1) * ldw + k) * eb, ospan = ((d - 1) * ldo + k) * eb;
+  if (wb != ob && wb < ob + ospan && ob < wb + wspan) return LORA_ERR_ARG;
+  if (wb == ob && ldw != ldo) return LORA_ERR_ARG;
+  MergeArgs m{};
+  m.dtype = dtype == LORA_DTYPE_BF16 ? 1 : 0;
+  m.d = d;
+  m.k = k;
+  m.W = wb;
+  m.ldw = ldw;
+  m.Wo = (uint8_t *)W_out;
+  m.ldo = ldo;
+  m.ar = make_ref(adapters, k, d, (int32_t)eb);
+  m.ranks = adapters->ranks;
+  m.scales = scales;
+  m.adapter = adapter;
+  m.coef = coef;
+  m.rp = (adapters->max_rank + 31) & ~31;
+  m.n_pages = adapters->n_pages;
+  return launch_merge(m, (hipStream_t)stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 lora_status_t lora_translate(const lora_adapters_t *adapters, const int32_t *adapter,
                              const int64_t *logical_off, int64_t n, int64_t *phys_off,
                              void *stream) {

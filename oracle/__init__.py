@@ -73,6 +73,8 @@ def _load():
     lib.oracle_lora_linear.argtypes = [i64, i64, i64, p, p, i32, p, i32, p, p, p, p, p, p,
                                        p, i32]
     lib.oracle_lora_linear.restype = None
+    lib.oracle_merge.argtypes = [i64, i64, i64, p, p, p, ctypes.c_double, ctypes.c_double, p, i32]
+    lib.oracle_merge.restype = None
     lib.oracle_threads.argtypes = [i32]
     lib.oracle_threads.restype = i32
     _lib = lib
@@ -211,3 +213,19 @@ def lora_linear(x, W, A_list, B_list, scales, ids, max_rank: int | None = None,
                                _ptr(a_off), _ptr(b_off), _ptr(A), _ptr(B), _ptr(sc), _ptr(ids_),
                                _ptr(y), nt)
     return y
+
+
+def merge(W, A, B, scale: float, coef: float = 1.0, n_threads: int | None = None) -> np.ndarray:
+    """W + coef * scale * B A in fp64 (W [d,k], A [r,k], B [d,r])."""
+    W64, A64, B64 = _f64(W), _f64(A), _f64(B)
+    d, k = W64.shape
+    r = A64.shape[0] if A64.ndim == 2 else 0
+    if A64.shape != (r, k) or B64.shape != (d, r):
+        raise ValueError("A must be [r,%d] and B [%d,r]" % (k, d))
+    if r == 0:
+        A64, B64 = np.zeros(1), np.zeros(1)
+    out = np.empty((d, k), np.float64)
+    nt = default_threads() if n_threads is None else int(n_threads)
+    _load().oracle_merge(d, k, r, _ptr(W64), _ptr(np.ascontiguousarray(A64)),
+                         _ptr(np.ascontiguousarray(B64)), float(scale), float(coef), _ptr(out), nt)
+    return out

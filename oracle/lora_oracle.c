@@ -27,7 +27,7 @@
 #include <omp.h>
 #endif
 
-/* ORACLE_MUTANT plants one deliberate mistake (1..9) so the test suite can
+/* ORACLE_MUTANT plants one deliberate mistake (1..12) so the test suite can
  * show that its pins catch it; the normal build leaves it at 0.  Only the
  * pin tests build mutants, into a temporary directory. */
 #ifndef ORACLE_MUTANT
@@ -252,6 +252,36 @@ void oracle_lora_linear(int64_t M, int64_t k, int64_t d, const double *x, const 
       y[m * d + n] = base - scales[s] * delta;
 #else
       y[m * d + n] = base + scales[s] * delta;
+#endif
+    }
+  }
+}
+
+/* Merged weight of one adapter: out[n][c] = W[n][c] + coef * scale *
+ * sum_j B[n][j] A[j][c] (j ascending), W and out d x k, A r x k, B d x r.
+ * "Your LoRA Adapters Are Thrashing Your GPUs", section 02 (weight merging vs
+ * keeping adapters separate): W' = W + (alpha/r) B A serves that adapter with
+ * the plain layer; coef = -1 takes it back out. */
+void oracle_merge(int64_t d, int64_t k, int64_t r, const double *W, const double *A,
+                  const double *B, double scale, double coef, double *out, int32_t n_threads) {
+  if (n_threads < 1) n_threads = 1;
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+  for (int64_t n = 0; n < d; ++n) {
+    for (int64_t c = 0; c < k; ++c) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < r; ++j) {
+#if ORACLE_MUTANT == 11 /* planted: A read as k x r (transposed) */
+        acc += B[n * r + j] * A[c * r + j];
+#else
+        acc += B[n * r + j] * A[j * k + c];
+#endif
+      }
+#if ORACLE_MUTANT == 10 /* planted: coef ignored */
+      out[n * k + c] = W[n * k + c] + scale * acc;
+#elif ORACLE_MUTANT == 12 /* planted: scale dropped */
+      out[n * k + c] = W[n * k + c] + coef * acc;
+#else
+      out[n * k + c] = W[n * k + c] + coef * scale * acc;
 #endif
     }
   }

@@ -283,9 +283,48 @@ def check_params(oracle):
         assert np.float32(e["alpha"]) / np.float32(e["r"]) == np.float32(e["scale"])
 
 
+def check_merge_identity(oracle):
+    """x W'^T with W' = merge(W, A_s, B_s, scale_s) equals the layer on rows of
+    adapter s (merging is exact in real arithmetic; fp64 rounding only)."""
+    w = wl.u1_scales()
+    p = w.projections[0]
+    for s in range(w.S):
+        Wm = oracle.merge(p.W, p.A[s], p.B[s], float(w.scales[s]))
+        ids = np.full(w.M, s, np.int32)
+        y = oracle_y(oracle, w, p, ids=ids)
+        err = normwise(w.x.double().numpy() @ Wm.T, y)
+        assert err <= 1e-12, "merged weight vs layer, adapter %d: %g" % (s, err)
+
+
+def check_merge_unmerge(oracle):
+    w = wl.c0_tiny_fp32()
+    p = w.projections[0]
+    W = p.W.double().numpy()
+    Wm = oracle.merge(W, p.A[1], p.B[1], float(w.scales[1]), coef=1.0)
+    assert np.max(np.abs(Wm - W)) > 1e-3
+    back = oracle.merge(Wm, p.A[1], p.B[1], float(w.scales[1]), coef=-1.0)
+    assert np.max(np.abs(back - W)) <= 1e-14
+    z = oracle.merge(W, np.zeros((0, W.shape[1])), np.zeros((W.shape[0], 0)), 3.0)
+    assert np.array_equal(z, W)  # rank 0 changes nothing
+
+
+def check_merge_hand(oracle):
+    # W = [[1, 2], [3, 4]], A = [[1, 0]] (r = 1), B = [[1], [2]], scale 0.5:
+    # B A = [[1, 0], [2, 0]] -> W' = [[1.5, 2], [4, 4]]; coef -2 -> [[0, 2], [1, 4]]
+    W = np.array([[1.0, 2.0], [3.0, 4.0]])
+    A = np.array([[1.0, 0.0]])
+    B = np.array([[1.0], [2.0]])
+    assert np.array_equal(oracle.merge(W, A, B, 0.5), np.array([[1.5, 2.0], [4.0, 4.0]]))
+    assert np.array_equal(oracle.merge(W, A, B, 0.5, coef=-2.0), np.array([[0.0, 2.0], [1.0, 4.0]]))
+    # rectangular: A = [[0, 1, 0]] (r = 1, k = 3), B = [[2]] (d = 1): W' = W + s * [0, 2, 0]
+    W2 = np.array([[1.0, 1.0, 1.0]])
+    assert np.array_equal(oracle.merge(W2, np.array([[0.0, 1.0, 0.0]]), np.array([[2.0]]), 0.25),
+                          np.array([[1.0, 1.5, 1.0]]))
+
+
 ALL_CHECKS = [
     check_merged_c0, check_merged_u1, check_merged_rect, check_none_rows, check_zero_b,
     check_hand_example, check_row_permutation, check_slot_relabel, check_plan_bruteforce,
     check_plan_hand, check_plan_pages, check_translate_closed_form, check_pool_roundtrip,
-    check_params,
+    check_params, check_merge_identity, check_merge_unmerge, check_merge_hand,
 ]

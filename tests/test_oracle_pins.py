@@ -24,6 +24,9 @@ MUTANTS = {
     7: "none rows take adapter 0",
     8: "last rank term dropped",
     9: "segment length off by one",
+    10: "merge ignores coef",
+    11: "merge reads A transposed",
+    12: "merge drops the scale",
 }
 
 
