@@ -282,7 +282,31 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
   }
 }
 
-template <int RB, int ECB>
+// Keep the first `keep` bf16 elements of a 16-byte fragment, zero the rest
+// (ranks at or past r: slot padding may hold anything).  Branch-free.
+__device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int keep) {
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t msk = 2 * i + 1 < keep ? 0xffffffffu : (2 * i < keep ? 0xffffu : 0u);
+    o[i] = q[i] & msk;
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// FAST: every slice in slots with max_rank % 8 == 0 (16-byte B rows), y
+// 16-byte aligned with every slice's columns a multiple of 8 wide and at a
+// multiple of 8.  Then the B fragments, the item's row numbers, the y runs
+// and the k-split partials are all loaded unconditionally at clamped
+// addresses and masked by selects afterwards, so they leave back to back
+// (loads under a branch -- even a uniform one -- or behind a slot/pool
+// address branch each sat in their own block behind a full wait: 18.5 ->
+// 16.2 us at the 70B q+v shapes).  The shrink keeps its masked loads: it is
+// bound by the address path of the vector memory unit, where clamped lanes
+// cost as much as real ones (measured slower with clamping).
+template <int RB, int ECB, bool FAST>
 __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   constexpr int RBK = RB / 16;
   constexpr int KP = RMAX_MFMA + 8;  // padded LDS row (bf16)
@@ -343,6 +367,16 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int64_t n = n0 + (wave * CB + cb) * 16 + (lane & 15);
+      if constexpr (FAST) {
+        // a rank chunk past the rank loads chunk 0's vector (same lines)
+        const bool ok = ks * 32 < kp && n < sl.d && jl < r;
+        const bool ok0 = n < sl.d && jl - ks * 32 < r;
+        const int64_t na = ok || ok0 ? n : n0;
+        const int ja = ok ? jl : (ok0 ? jl - ks * 32 : 0);
+        const bf16x8_t v = ld16(ar.B + (((int64_t)it.adapter * ar.d + na) * ar.max_rank + ja) * 2);
+        fb[ks][cb] = keep_first(v, ok ? r - jl : 0);
+        continue;
+      }
       bf16x8_t v = zero8();
       if (ks * 32 < kp && n < sl.d && jl < r) {
         if (bvec && jl + 8 <= r) {
@@ -374,8 +408,28 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   uint16_t *yb = reinterpret_cast<uint16_t *>(a.y) + sl.col0;
   uint16_t *yp[YCH];
   uint4 yv[YCH];
+  if constexpr (FAST) {
+    // row numbers first (one batch of loads), then the y runs
+    int rows[YCH];
 #pragma unroll
-  for (int c = 0; c < YCH; ++c) {
+    for (int c = 0; c < YCH; ++c) {
+      const int ch = (c / CPT) * 16 * CPR + tid + (c % CPT) * 256;
+      const int row = ch / CPR;
+      rows[c] = item_row<RB == 16>(ix, perm, it, row < nr ? row : 0);
+    }
+#pragma unroll
+    for (int c = 0; c < YCH; ++c) {
+      const int ch = (c / CPT) * 16 * CPR + tid + (c % CPT) * 256;
+      const int row = ch / CPR;
+      const int64_t n = n0 + (ch % CPR) * 8;
+      const bool ok = row < nr && n < sl.d;
+      uint16_t *p = yb + (int64_t)rows[c] * a.ldy + (ok ? n : n0);
+      yv[c] = *reinterpret_cast<const uint4 *>(p);
+      yp[c] = ok ? p : nullptr;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < (FAST ? 0 : YCH); ++c) {
     const int ch = (c / CPT) * 16 * CPR + tid + (c % CPT) * 256;  // pass c / CPT
     const int row = ch / CPR;
     const int64_t n = n0 + (ch % CPR) * 8;
@@ -400,7 +454,16 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
     const int row = e / kp4;
     const int j = (e - row * kp4) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < nr && j < r) {
+    if constexpr (FAST) {
+      const bool ok = row < nr && j < r;
+      v = tpart_sum4(tpart, it.pos + (ok ? row : 0), slice, ok ? j : 0, a.ksplit, a.L.rows,
+                     a.n_slices, a.L.R);
+      // entries past the rank are never written by the shrink
+      v.x = ok ? v.x : 0.f;
+      v.y = ok && j + 1 < r ? v.y : 0.f;
+      v.z = ok && j + 2 < r ? v.z : 0.f;
+      v.w = ok && j + 3 < r ? v.w : 0.f;
+    } else if (row < nr && j < r) {
       v = tpart_sum4(tpart, it.pos + row, slice, j, a.ksplit, a.L.rows, a.n_slices, a.L.R);
       // entries past the rank are never written by the shrink
       if (j + 1 >= r) v.y = 0.f;
@@ -471,7 +534,7 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) e8[q] = f32_to_bf16_bits(bf16_bits_to_f32(old[q]) + scale * sv[q]);
       const int64_t n = n0 + col;
-      if (yvec && n + 8 <= sl.d) {
+      if (FAST || (yvec && n + 8 <= sl.d)) {
         *reinterpret_cast<uint4 *>(yp[c]) = __builtin_bit_cast(uint4, e8);
       } else {
         for (int q = 0; q < 8; ++q)
@@ -504,12 +567,18 @@ hipError_t launch_expand_sgmv(const LoraArgs &a0, int rows_per_item, hipStream_t
     a.col_blk[q + 1] = a.col_blk[q] + (int32_t)((a.sl[q].d + ecb - 1) / ecb);
   // one dimension: item-major, column blocks padded to a multiple of 8
   const int64_t cb8 = ((int64_t)a.col_blk[a.n_slices] + 7) / 8 * 8;
+  bool fast = a.y_vec != 0;
+  for (int q = 0; q < a.n_slices; ++q)
+    fast = fast && !a.sl[q].ar.pooled && a.sl[q].ar.max_rank % 8 == 0 && a.sl[q].d % 8 == 0 &&
+           a.sl[q].col0 % 8 == 0;
   if (rows_per_item == 16) {
     const dim3 grid((unsigned)(a.L.items_g_cap * cb8));
-    hipLaunchKernelGGL((k_expand_mfma<16, kExpandCols16>), grid, dim3(256), 0, st, a);
+    if (fast) hipLaunchKernelGGL((k_expand_mfma<16, kExpandCols16, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_expand_mfma<16, kExpandCols16, false>), grid, dim3(256), 0, st, a);
   } else {
     const dim3 grid((unsigned)(a.L.items_s_cap * cb8));
-    hipLaunchKernelGGL((k_expand_mfma<64, 256>), grid, dim3(256), 0, st, a);
+    if (fast) hipLaunchKernelGGL((k_expand_mfma<64, 256, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_expand_mfma<64, 256, false>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

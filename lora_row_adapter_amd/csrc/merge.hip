@@ -173,13 +173,6 @@ __device__ __forceinline__ void merge_astage(uint16_t *At, const uint4 (&a)[4]) 
   }
 }
 
-// Two floats to a packed bf16 pair, round to nearest even (one
-// v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 template <bool POOL, bool BVEC>
 __global__ __launch_bounds__(256) void k_merge_bf16(MergeArgs m) {
   __shared__ __attribute__((aligned(16))) uint16_t At[kTC * kAtP];
