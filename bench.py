@@ -21,6 +21,7 @@ Prints one JSON line (rank 0):
   adapter_activation = host-to-device loading of the same adapters through
                the pool manager (GB/s against the PCIe 5.0 x16 link)
   merge      = lora_merge (W' = W + s B A) at the q and v shapes, HBM GB/s
+  quantized_base = the same step over INT8 / INT4 base weights
 """
 import argparse
 import hashlib
@@ -62,6 +63,8 @@ def parse():
                     help="skip the adapter-activation (host-to-device) measurement")
     ap.add_argument("--no-merge", action="store_true",
                     help="skip the merged-weight (lora_merge) measurement")
+    ap.add_argument("--no-quant", action="store_true",
+                    help="skip the INT8 / INT4 base-weight measurement")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/ summaries from a rocprofv3 run whose trace/, fetch/, "
                          "write/, cfetch/, cwrite/ output directories are under DIR, and exit")
@@ -249,9 +252,51 @@ def main():
         result["adapter_activation"] = adapter_activation(lr, w, pq, pv, stream)
     if not args.no_merge:
         result["merge"] = merge_rate(lr, w, pq, pv, sets, stream)
+    if not args.no_quant:
+        result["quantized_base"] = quantized_rate(lr, wl, w, sets, ids, ws, stream, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, pq, pv, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def quantized_rate(lr, wl, w, sets, ids, ws, stream, args):
+    """The same q+v step over an INT8 (per-row scales) and an INT4 (per-row,
+    per-128-k-group scales) stacked base weight: lora_linear_sliced_q with
+    the buffer sets' x, adapters and outputs, each set with its own
+    quantized weight copy; tokens/s and the base GEMM's event-timed launch."""
+    out = {}
+    M = w.M
+    steps = max(100, args.steps // 2)
+    for fmt, group in (("int8", 0), ("int4", 128)):
+        q, s = wl.quantized_base(w, fmt, group=group or 128, names=["q", "v"])
+        code = lr.W_INT8 if fmt == "int8" else lr.W_INT4
+        qws = [lr.QWeight(code, q.cuda(), s.cuda(), w.k, group=group) for _ in range(len(sets))]
+
+        def step(i):
+            st_ = sets[i % len(sets)]
+            lr.lora_linear_sliced_q(st_["x"], qws[i % len(qws)], st_["slices"], ids, y=st_["y"],
+                                    workspace=ws, stream=stream)
+        for i in range(max(200, args.warmup // 4)):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        with lr.Profiler():
+            for i in range(200):
+                step(i)
+            prof = lr.Profiler.read(reset=True)
+            torch.cuda.synchronize()
+        gemm_us = prof["gemm"]["ms"] * 1e3 / max(prof["gemm"]["launches"], 1)
+        flops = 2.0 * M * q.shape[0] * w.k
+        wbytes = q.numel() + s.numel() * 4
+        out[fmt] = {"tokens_per_s": round(M * steps / el, 1), "ms_per_step": round(el * 1e3 / steps, 4),
+                    "gemm_us": round(gemm_us, 2), "gemm_tflops": round(flops / gemm_us / 1e6, 1),
+                    "weight_bytes": int(wbytes), "group": group or None}
+    log("quantized base: " + json.dumps(out))
+    return out
 
 
 def merge_rate(lr, w, pq, pv, sets, stream, reps=20):

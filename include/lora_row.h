@@ -207,6 +207,52 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
                                  int32_t path, uint32_t flags, void *stream);
 
 /*
+ * Quantized base weight (bf16 activations and adapters; the base GEMM
+ * dequantizes on the fly).  "Your LoRA Adapters Are Thrashing Your GPUs",
+ * section 02: production deployments quantize the base model to INT4 or INT8
+ * and keep the LoRA weights in 16 bits.  Symmetric formats (no zero point):
+ *   LORA_W_INT8: q int8 [d, ldq bytes], scales fp32 [d]:
+ *       W[n, j] = scales[n] * q[n, j]; the scale multiplies the fp32 dot
+ *       product (the dequantized weight is exact).
+ *   LORA_W_INT4: q two's-complement 4-bit values, two per byte, element 2i of
+ *       a row in the low nibble of byte i, element 2i + 1 in the high nibble;
+ *       scales fp32 [d, k / group]:
+ *       W[n, j] = scales[n * (k / group) + j / group] * q[n, j]; each
+ *       q * scale is rounded once to bf16 before the MFMA.
+ * group: INT4 k-group, a multiple of 64 that divides k (INT8: ignored).
+ * ldq: row stride in bytes, a multiple of 16, >= k (INT8) or k / 2 (INT4).
+ * q and scales are device memory; q 16-byte aligned.  k % 64 == 0.
+ */
+typedef enum lora_wformat {
+  LORA_W_INT8 = 1,
+  LORA_W_INT4 = 2
+} lora_wformat_t;
+
+typedef struct lora_qweight {
+  int32_t format;       /* lora_wformat_t */
+  int32_t group;        /* INT4 k-group size */
+  const void *q;        /* device, packed weights [d, ldq] */
+  int64_t ldq;          /* bytes */
+  const float *scales;  /* device fp32: INT8 [d]; INT4 [d, k / group] */
+} lora_qweight_t;
+
+/* y = x dequant(W)^T, bf16 x [M, k] and y [M, d] (as lora_gemm). */
+lora_status_t lora_gemm_q(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
+                          const lora_qweight_t *W, void *y, int64_t ldy, void *stream);
+
+/*
+ * lora_linear_sliced with a quantized base weight: W stacks the slices'
+ * quantized weights by rows ([sum_i d_i] rows, scales stacked alike); the
+ * adapters, ids, workspace (lora_workspace_bytes_sliced with bf16) and every
+ * other argument as in lora_linear_sliced.  bf16 only.
+ */
+lora_status_t lora_linear_sliced_q(int64_t M, int64_t k, const void *x, int64_t ldx,
+                                   const lora_qweight_t *W, int32_t n_slices,
+                                   const lora_slice_t *slices, const int32_t *adapter_ids, void *y,
+                                   int64_t ldy, void *workspace, size_t workspace_bytes,
+                                   int32_t path, uint32_t flags, void *stream);
+
+/*
  * The plan step alone (what lora_linear runs first): classify rows, sort
  * the adapted rows by (adapter, row) -- stable -- and build the segment
  * table.  "Adapter Residency ...", "Batch composition under many adapters":

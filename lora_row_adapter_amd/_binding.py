@@ -75,6 +75,16 @@ class _CProfile(ctypes.Structure):
     ]
 
 
+class _CQWeight(ctypes.Structure):
+    _fields_ = [
+        ("format", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("ldq", ctypes.c_int64),
+        ("scales", ctypes.c_void_p),
+    ]
+
+
 class _CPoolDesc(ctypes.Structure):
     _fields_ = [
         ("pool", ctypes.c_void_p),
@@ -141,6 +151,12 @@ def load_library():
     lib.lora_plan.restype = i32
     lib.lora_plan_view.argtypes = [p, sz, i64, pad, ctypes.POINTER(_CPlanView)]
     lib.lora_plan_view.restype = i32
+    pqw = ctypes.POINTER(_CQWeight)
+    lib.lora_gemm_q.argtypes = [i64, i64, i64, p, i64, pqw, p, i64, p]
+    lib.lora_gemm_q.restype = i32
+    lib.lora_linear_sliced_q.argtypes = [i64, i64, p, i64, pqw, i32, ctypes.POINTER(_CSlice), p, p,
+                                         i64, p, sz, i32, u32, p]
+    lib.lora_linear_sliced_q.restype = i32
     lib.lora_merge.argtypes = [i32, i64, i64, p, i64, pad, i32, p, ctypes.c_float, p, i64, p]
     lib.lora_merge.restype = i32
     lib.lora_translate.argtypes = [pad, p, p, i64, p, p]
@@ -580,6 +596,77 @@ def lora_plan_view(workspace: torch.Tensor, M: int, adapters: Adapters) -> dict:
         "perm": arr(v.perm, n_ad), "seg_adapter": arr(v.seg_adapter, n_seg),
         "seg_start": arr(v.seg_start, n_seg), "seg_len": arr(v.seg_len, n_seg),
     }
+
+
+W_INT8, W_INT4 = 1, 2
+
+
+class QWeight:
+    """A quantized base weight (include/lora_row.h, lora_qweight_t): packed
+    q as a device uint8 tensor [d, ldq bytes] and fp32 scales ([d] for INT8,
+    [d, k / group] for INT4)."""
+
+    def __init__(self, fmt: int, q: torch.Tensor, scales: torch.Tensor, k: int, group: int = 0):
+        if q.dtype not in (torch.uint8, torch.int8) or q.dim() != 2:
+            raise TypeError("q must be a 2-D uint8 / int8 tensor")
+        if q.stride(1) != 1:
+            raise ValueError("q rows must be contiguous")
+        self.fmt, self.q, self.scales, self.k, self.group = int(fmt), q, scales, int(k), int(group)
+        self.d = int(q.shape[0])
+        c = _CQWeight()
+        c.format = self.fmt
+        c.group = self.group
+        if not q.is_cuda:
+            raise ValueError("q must be a device tensor")
+        c.q = q.data_ptr()
+        c.ldq = q.stride(0) * q.element_size()
+        c.scales = _dev(scales, "scales", torch.float32)
+        self._c = c
+
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def lora_gemm_q(x: torch.Tensor, W: QWeight, y: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """y = x dequant(W)^T (bf16 x and y)."""
+    lib = load_library()
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if y is None:
+        y = torch.empty((x.shape[0], W.d), dtype=x.dtype, device=x.device)
+    xp, ldx = _rows(x, "x")
+    yp, ldy = _rows(y, "y")
+    _check(lib.lora_gemm_q(x.shape[0], x.shape[1], W.d, xp, ldx, W.ref(), yp, ldy,
+                           _stream_ptr(stream)), "lora_gemm_q")
+    return y
+
+
+def lora_linear_sliced_q(x: torch.Tensor, W: QWeight, slices, adapter_ids: torch.Tensor,
+                         y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         path: int = PATH_AUTO, flags: int = 0, stream=None) -> torch.Tensor:
+    """lora_linear_sliced over a quantized stacked base weight (bf16)."""
+    lib = load_library()
+    M, k = x.shape
+    d_total = sum(sl.d for sl in slices)
+    if W.d != d_total:
+        raise ValueError("W must stack the slices' weights: %d rows expected" % d_total)
+    if y is None:
+        y = torch.empty((M, d_total), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes_sliced(M, k, x.dtype, slices), dtype=torch.uint8,
+                                device=x.device)
+    xp, ldx = _rows(x, "x")
+    yp, ldy = _rows(y, "y")
+    if adapter_ids.numel() != M:
+        raise ValueError("adapter_ids must have one entry per row")
+    arr = _slice_array(slices)
+    st = lib.lora_linear_sliced_q(M, k, xp, ldx, W.ref(), len(slices), arr,
+                                  _dev(adapter_ids, "adapter_ids", torch.int32), yp, ldy,
+                                  _dev(workspace, "workspace"), workspace.numel(), int(path),
+                                  int(flags), _stream_ptr(stream))
+    _check(st, "lora_linear_sliced_q")
+    return y
 
 
 def lora_merge(W: torch.Tensor, adapters: Adapters, adapter: int, scales: torch.Tensor,

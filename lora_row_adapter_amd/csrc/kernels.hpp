@@ -70,6 +70,23 @@ hipError_t launch_translate(const AdapterRef &ar, int32_t S, int64_t n_pages,
 // Base GEMM y = x W^T (bf16 operands: MFMA tiles; fp32: VALU).
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, hipStream_t st);
+// Base GEMM with a quantized weight (bf16 x and y).
+struct QGemmArgs {
+  int32_t fmt;  // 1 INT8 (per-row scales), 2 INT4 (per-row, per-k-group scales)
+  int M, N, K;
+  const uint16_t *x;
+  int64_t ldx;            // elements
+  const uint8_t *q;
+  int64_t ldq;            // bytes
+  const float *scales;    // INT8 [N]; INT4 [N, ngroups]
+  int32_t group;          // INT4 k-group (multiple of 64)
+  int32_t ngroups;        // INT4: K / group; INT8: 1
+  uint16_t *y;
+  int64_t ldy;
+  int tiles_m, tiles_n;
+  int vec_store;
+};
+hipError_t launch_gemm_q(const QGemmArgs &a, hipStream_t st);
 hipError_t launch_shrink_gather(const LoraArgs &a, hipStream_t st);
 hipError_t launch_expand_gather(const LoraArgs &a, hipStream_t st);
 hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_slice,

@@ -213,6 +213,58 @@ static lora_status_t check_gemm_args(lora_dtype_t dt, int64_t M, int64_t k, int6
   return LORA_OK;
 }
 
+// Quantized base weight: host checks and kernel arguments.
+static lora_status_t check_qweight(const lora_qweight_t *W, int64_t k, int64_t d) {
+  if (W == nullptr || W->q == nullptr || W->scales == nullptr) return LORA_ERR_ARG;
+  if (W->format != LORA_W_INT8 && W->format != LORA_W_INT4) return LORA_ERR_DTYPE;
+  if (!aligned16(W->q) || W->ldq % 16 != 0) return LORA_ERR_SHAPE;
+  if (W->format == LORA_W_INT8 && W->ldq < k) return LORA_ERR_SHAPE;
+  if (W->format == LORA_W_INT4) {
+    if (W->ldq < k / 2) return LORA_ERR_SHAPE;
+    if (W->group < 64 || W->group % 64 != 0 || k % W->group != 0) return LORA_ERR_SHAPE;
+  }
+  // byte offsets inside one tile's rows and scales stay below 2^32
+  const int64_t ng = W->format == LORA_W_INT4 ? k / W->group : 1;
+  if ((uint64_t)144 * W->ldq >= (1ull << 32) || (uint64_t)144 * ng * 4 >= (1ull << 32))
+    return LORA_ERR_SHAPE;
+  (void)d;
+  return LORA_OK;
+}
+
+static lora_status_t check_q_gemm_args(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
+                                       const lora_qweight_t *W, const void *y, int64_t ldy) {
+  if (M < 0 || k < 1 || d < 1) return LORA_ERR_SHAPE;
+  if (M > INT32_MAX || k > INT32_MAX || d > INT32_MAX) return LORA_ERR_SHAPE;
+  lora_status_t s = check_qweight(W, k, d);
+  if (s != LORA_OK) return s;
+  if (M == 0) return LORA_OK;
+  if (x == nullptr || y == nullptr) return LORA_ERR_ARG;
+  if (ldx < k || ldy < d) return LORA_ERR_SHAPE;
+  if (k % 64 != 0 || ldx % 8 != 0 || !aligned16(x)) return LORA_ERR_SHAPE;
+  if ((uint64_t)256 * ldx * 2 >= (1ull << 32)) return LORA_ERR_SHAPE;
+  return LORA_OK;
+}
+
+static QGemmArgs make_q_args(const lora_qweight_t *W, int64_t M, int64_t k, int64_t d,
+                             const void *x, int64_t ldx, void *y, int64_t ldy) {
+  QGemmArgs a{};
+  a.fmt = W->format == LORA_W_INT8 ? 1 : 2;
+  a.M = (int)M;
+  a.N = (int)d;
+  a.K = (int)k;
+  a.x = (const uint16_t *)x;
+  a.ldx = ldx;
+  a.q = (const uint8_t *)W->q;
+  a.ldq = W->ldq;
+  a.scales = W->scales;
+  a.group = W->format == LORA_W_INT4 ? W->group : 64;
+  a.ngroups = W->format == LORA_W_INT4 ? (int32_t)(k / W->group) : 1;
+  a.y = (uint16_t *)y;
+  a.ldy = ldy;
+  a.vec_store = ((ldy % 8) == 0 && ((uintptr_t)y & 15) == 0) ? 1 : 0;
+  return a;
+}
+
 }  // namespace lora
 
 using namespace lora;
@@ -287,6 +339,16 @@ lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, con
   hipError_t e = timed(LORA_K_GEMM, st, [&] {
     return launch_gemm(dtype, M, k, d, x, ldx, W, ldw, y, ldy, st);
   });
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status_t lora_gemm_q(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
+                          const lora_qweight_t *W, void *y, int64_t ldy, void *stream) {
+  lora_status_t s = check_q_gemm_args(M, k, d, x, ldx, W, y, ldy);
+  if (s != LORA_OK || M == 0) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const QGemmArgs a = make_q_args(W, M, k, d, x, ldx, y, ldy);
+  hipError_t e = timed(LORA_K_GEMM, st, [&] { return launch_gemm_q(a, st); });
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -373,17 +435,22 @@ lora_status_t lora_plan_view(const void *workspace, size_t workspace_bytes, int6
   return LORA_OK;
 }
 
-lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
-                                 int64_t ldx, const void *W, int64_t ldw, int32_t n_slices,
-                                 const lora_slice_t *slices, const int32_t *adapter_ids, void *y,
-                                 int64_t ldy, void *workspace, size_t workspace_bytes,
-                                 int32_t path, uint32_t flags, void *stream) {
+// The layer over several slices; the base weight is dense (W, ldw) or, with
+// qw != nullptr, quantized (bf16 only).
+static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
+                                        int64_t ldx, const void *W, int64_t ldw,
+                                        const lora_qweight_t *qw, int32_t n_slices,
+                                        const lora_slice_t *slices, const int32_t *adapter_ids,
+                                        void *y, int64_t ldy, void *workspace,
+                                        size_t workspace_bytes, int32_t path, uint32_t flags,
+                                        void *stream) {
   int32_t S = 0, R = 0;
   int64_t d_total = 0;
   if (slices == nullptr || n_slices < 1 || n_slices > LORA_MAX_SLICES) return LORA_ERR_ARG;
   lora_status_t s = check_slices(n_slices, slices, M, &S, &R, &d_total);
   if (s != LORA_OK) return s;
-  s = check_gemm_args(dtype, M, k, d_total, x, ldx, W, ldw, y, ldy);
+  s = qw ? check_q_gemm_args(M, k, d_total, x, ldx, qw, y, ldy)
+         : check_gemm_args(dtype, M, k, d_total, x, ldx, W, ldw, y, ldy);
   if (s != LORA_OK) return s;
   if (path != LORA_PATH_AUTO && path != LORA_PATH_GATHER && path != LORA_PATH_SGMV) return LORA_ERR_ARG;
   if ((flags & ~LORA_FLAG_REUSE_PLAN) != 0) return LORA_ERR_ARG;
@@ -487,6 +554,7 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
       if (fork && hipEventRecord(ev_join, ps) != hipSuccess) return LORA_ERR_HIP;
     }
     hipError_t e = timed(LORA_K_GEMM, st, [&] {
+      if (qw) return launch_gemm_q(make_q_args(qw, Mc, k, d_total, xc, ldx, yc, ldy), st);
       return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, st);
     });
     if (e != hipSuccess) return LORA_ERR_HIP;
@@ -505,6 +573,25 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
     }
   }
   return LORA_OK;
+}
+
+lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
+                                 int64_t ldx, const void *W, int64_t ldw, int32_t n_slices,
+                                 const lora_slice_t *slices, const int32_t *adapter_ids, void *y,
+                                 int64_t ldy, void *workspace, size_t workspace_bytes,
+                                 int32_t path, uint32_t flags, void *stream) {
+  return linear_sliced_impl(dtype, M, k, x, ldx, W, ldw, nullptr, n_slices, slices, adapter_ids,
+                            y, ldy, workspace, workspace_bytes, path, flags, stream);
+}
+
+lora_status_t lora_linear_sliced_q(int64_t M, int64_t k, const void *x, int64_t ldx,
+                                   const lora_qweight_t *W, int32_t n_slices,
+                                   const lora_slice_t *slices, const int32_t *adapter_ids, void *y,
+                                   int64_t ldy, void *workspace, size_t workspace_bytes,
+                                   int32_t path, uint32_t flags, void *stream) {
+  if (W == nullptr) return LORA_ERR_ARG;
+  return linear_sliced_impl(LORA_DTYPE_BF16, M, k, x, ldx, nullptr, 0, W, n_slices, slices,
+                            adapter_ids, y, ldy, workspace, workspace_bytes, path, flags, stream);
 }
 
 lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,

@@ -340,3 +340,33 @@ def algorithmic_bytes(w: Workload, proj: Projection) -> Dict[str, float]:
         "gemm_flops": 2.0 * M * d * k,
         "gemm_bytes": (M * k + d * k + M * d) * e,
     }
+
+
+def quantized_base(w: Workload, fmt: str, group: int = 128, names=None):
+    """Seeded quantized base weights for the workload's projections, stacked
+    by rows in `names` order (default: all).  Symmetric formats:
+      int8: q uniform in [-127, 127], one scale per row;
+      int4: q uniform in [-8, 7], two per byte (element 2i in the low nibble),
+            one scale per row and k-group.
+    Scales are sqrt(3 / k) / qmax times U(0.5, 1.5), so the weights have
+    about the variance 1/k of the bf16 workloads.  Draws come from
+    SeedSequence(20261202 + index + 104729); nothing is computed from the
+    bf16 weights.  Returns (q uint8 [d, ldq], scales float32: [d] for int8,
+    [d, k / group] for int4)."""
+    names = [p.name for p in w.projections] if names is None else list(names)
+    d = sum(w.proj(n).d for n in names)
+    k = w.k
+    rng = np.random.default_rng(np.random.SeedSequence(BASE_SEED + w.index + 104729))
+    if fmt == "int8":
+        q = rng.integers(-127, 128, size=(d, k), dtype=np.int64).astype(np.int8)
+        s = (np.sqrt(3.0 / k) / 127.0 * rng.uniform(0.5, 1.5, size=d)).astype(np.float32)
+        return torch.from_numpy(q.view(np.uint8).copy()), torch.from_numpy(s)
+    if fmt == "int4":
+        if k % group or group % 64:
+            raise ValueError("group must be a multiple of 64 dividing k")
+        v = rng.integers(-8, 8, size=(d, k), dtype=np.int64)
+        u = (v & 0xF).astype(np.uint8)
+        packed = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+        s = (np.sqrt(3.0 / k) / 8.0 * rng.uniform(0.5, 1.5, size=(d, k // group))).astype(np.float32)
+        return torch.from_numpy(packed), torch.from_numpy(s)
+    raise ValueError(fmt)

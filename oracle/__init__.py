@@ -229,3 +229,42 @@ def merge(W, A, B, scale: float, coef: float = 1.0, n_threads: int | None = None
     _load().oracle_merge(d, k, r, _ptr(W64), _ptr(np.ascontiguousarray(A64)),
                          _ptr(np.ascontiguousarray(B64)), float(scale), float(coef), _ptr(out), nt)
     return out
+
+
+def dequant_int8(q, scales) -> np.ndarray:
+    """W[n, j] = scales[n] * q[n, j] in fp64 (q int8 [d, k], scales [d]).
+
+    "Your LoRA Adapters Are Thrashing Your GPUs", section 02: an INT8 base
+    weight; the symmetric per-output-row reading."""
+    q = np.asarray(q)
+    if q.dtype != np.int8:
+        q = q.view(np.int8) if q.dtype == np.uint8 else q.astype(np.int8)
+    s = np.asarray(scales, np.float64).reshape(-1)
+    if s.size != q.shape[0]:
+        raise ValueError("one scale per row")
+    return q.astype(np.float64) * s[:, None]
+
+
+def unpack_int4(packed, k: int) -> np.ndarray:
+    """Signed 4-bit values of a packed row-major [d, >= k/2] byte array:
+    element 2i of a row is the low nibble of byte i, element 2i + 1 the high
+    nibble, both two's complement (-8 .. 7).  Returns int8 [d, k]."""
+    b = np.asarray(packed).astype(np.uint8)[:, : k // 2]
+    lo = (b & 0x0F).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty((b.shape[0], k), np.int8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def dequant_int4(packed, scales, group: int, k: int) -> np.ndarray:
+    """W[n, j] = scales[n, j // group] * q[n, j] in fp64.
+
+    "Your LoRA Adapters Are Thrashing Your GPUs", section 02: an INT4 base
+    weight; the symmetric reading with one scale per row and k-group."""
+    q = unpack_int4(packed, k).astype(np.float64)
+    s = np.asarray(scales, np.float64).reshape(q.shape[0], k // group)
+    return q * np.repeat(s, group, axis=1)

@@ -322,9 +322,38 @@ def check_merge_hand(oracle):
                           np.array([[1.0, 1.5, 1.0]]))
 
 
+def check_dequant_hand(oracle):
+    """Quantized base weights: hand-worked values of both formats."""
+    q8 = np.array([[1, -2, 0], [127, -128, 5]], np.int8)
+    got = oracle.dequant_int8(q8, [0.5, 2.0])
+    assert np.array_equal(got, np.array([[0.5, -1.0, 0.0], [254.0, -256.0, 10.0]]))
+    # bytes 0x21, 0xF8, 0x7F, 0x08: nibbles low then high -> 1, 2, -8, -1, -1, 7, -8, 0
+    packed = np.array([[0x21, 0xF8, 0x7F, 0x08]], np.uint8)
+    assert np.array_equal(oracle.unpack_int4(packed, 8),
+                          np.array([[1, 2, -8, -1, -1, 7, -8, 0]], np.int8))
+    # group 4: scales 1 and 10 for the two halves of the row
+    got = oracle.dequant_int4(packed, np.array([[1.0, 10.0]]), 4, 8)
+    assert np.array_equal(got, np.array([[1.0, 2.0, -8.0, -1.0, -10.0, 70.0, -80.0, 0.0]]))
+
+
+def check_int4_pack_roundtrip(oracle):
+    """Every value -8..7 in every nibble position survives packing by an
+    element-wise loop (written here) and the oracle's unpacking."""
+    rng = np.random.default_rng(4)
+    v = rng.integers(-8, 8, size=(5, 64))
+    v[0, :16] = np.arange(-8, 8)
+    packed = np.zeros((5, 32), np.uint8)
+    for n in range(5):
+        for j in range(64):
+            nib = int(v[n, j]) & 0xF
+            packed[n, j // 2] |= nib << (4 * (j % 2))
+    assert np.array_equal(oracle.unpack_int4(packed, 64), v.astype(np.int8))
+
+
 ALL_CHECKS = [
     check_merged_c0, check_merged_u1, check_merged_rect, check_none_rows, check_zero_b,
     check_hand_example, check_row_permutation, check_slot_relabel, check_plan_bruteforce,
     check_plan_hand, check_plan_pages, check_translate_closed_form, check_pool_roundtrip,
     check_params, check_merge_identity, check_merge_unmerge, check_merge_hand,
+    check_dequant_hand, check_int4_pack_roundtrip,
 ]
