@@ -6,7 +6,10 @@ of one attention layer, for 512 rows with 12 adapters of rank {4 x3, 16 x6,
 64 x3} (alpha = 2r, Zipf 1.1 popularity, 10% rows without adapter), bf16
 with fp32 accumulation.  Both projections share x and the per-row adapter
 ids, so they run as one multi-slice call: plan, one base GEMM over the
-stacked [9216, 8192] weight, one shrink (x read once), one expand.
+stacked [9216, 8192] weight that also computes the shrink (t = x A^T for
+every adapter rank, folded into its tiles), one expand.  The shrink as its
+own kernel (x read once for both slices) is timed in a second pass with the
+folding turned off (kernels.separate_shrink_step, kernels.shrink_gbs).
 
 Inputs are seeded synthetic tensors already resident in HBM.  The step
 rotates over several independent buffer sets (x, W_q, W_v, adapter slots,
@@ -17,6 +20,7 @@ Prints one JSON line (rank 0):
   value      = tokens/s through the (q + v) pair = 512 * steps / elapsed
   roofline   = base GEMM (the dominant kernel) MFMA TFLOP/s vs the bf16 peak,
                from per-launch HIP events recorded on the launch stream
+               (with the shrink folded in, its flops count too)
   cpu_baseline = the fp64 oracle on a bounded row sample, on the host cores
   adapter_activation = host-to-device loading of the same adapters through
                the pool manager (GB/s against the PCIe 5.0 x16 link)
@@ -145,10 +149,21 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i, flags=0):
         s = sets[i % len(sets)]
         lr.lora_linear_sliced(s["x"], s["W"], s["slices"], ids, y=s["y"], workspace=ws, path=path,
-                              stream=stream)
+                              flags=flags, stream=stream)
+
+    def profiled(n, flags=0):
+        """n steps under the library's per-launch events (library-side, on
+        the launch stream); kernel class -> {ms, launches}, wall seconds."""
+        with lr.Profiler():
+            t1 = time.perf_counter()
+            for i in range(n):
+                step(i, flags)
+            prof = lr.Profiler.read(reset=True)
+            torch.cuda.synchronize()
+            return prof, time.perf_counter() - t1
 
     for i in range(args.warmup):
         step(i)
@@ -168,13 +183,7 @@ def main():
     # launch stream) for per-kernel durations
     # (at most 400 steps: the library's event ring holds 8192 launches)
     prof_steps = min(args.steps, 400)
-    with lr.Profiler():
-        t1 = time.perf_counter()
-        for i in range(prof_steps):
-            step(i)
-        prof = lr.Profiler.read(reset=True)
-        torch.cuda.synchronize()
-        ev_elapsed = time.perf_counter() - t1
+    prof, ev_elapsed = profiled(prof_steps)
     per = {kname: prof[kname]["ms"] * 1e3 / max(prof[kname]["launches"], 1)
            for kname in lr.KERNEL_CLASSES}
     launches = {kname: prof[kname]["launches"] for kname in lr.KERNEL_CLASSES}
@@ -182,17 +191,39 @@ def main():
 
     bq = wl.algorithmic_bytes(w, pq)
     bv = wl.algorithmic_bytes(w, pv)
+    # no shrink launch: the library folded the shrink into the base GEMM,
+    # which then also does the shrink's algorithmic work
+    folded = prof["shrink"]["launches"] + prof["sgmv_shrink"]["launches"] == 0
     gemm_flops = bq["gemm_flops"] + bv["gemm_flops"]
+    gemm_alg_flops = gemm_flops + (bq["shrink_flops"] + bv["shrink_flops"] if folded else 0.0)
     gemm_us_step = prof["gemm"]["ms"] * 1e3 / prof_steps
-    gemm_tflops = gemm_flops / (gemm_us_step * 1e-6) / 1e12
-    shrink_us_step = (prof["shrink"]["ms"] + prof["sgmv_shrink"]["ms"]) * 1e3 / prof_steps
+    gemm_tflops = gemm_alg_flops / (gemm_us_step * 1e-6) / 1e12
     expand_us_step = (prof["expand"]["ms"] + prof["sgmv_expand"]["ms"]) * 1e3 / prof_steps
-    # the fused shrink reads x once for both projections
-    x_bytes = bq["M_a"] * k * 2
-    shrink_bytes = bq["shrink_bytes"] + bv["shrink_bytes"] - x_bytes
-    shrink_gbs = shrink_bytes / (shrink_us_step * 1e-6) / 1e9
     expand_gbs = (bq["expand_bytes"] + bv["expand_bytes"]) / (expand_us_step * 1e-6) / 1e9
     kernel_us_step = sum(prof[kname]["ms"] for kname in lr.KERNEL_CLASSES) * 1e3 / prof_steps
+    # the shrink as its own kernel: the same steps with the folding turned off
+    # (the multi-slice shrink reads x once for both projections)
+    x_bytes = bq["M_a"] * k * 2
+    shrink_bytes = bq["shrink_bytes"] + bv["shrink_bytes"] - x_bytes
+    for i in range(min(args.warmup, 500)):
+        step(i, lr.FLAG_SEPARATE_SHRINK)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(prof_steps):
+        step(i, lr.FLAG_SEPARATE_SHRINK)
+    torch.cuda.synchronize()
+    sep_ms = (time.perf_counter() - t2) * 1e3 / prof_steps
+    sprof, _ = profiled(prof_steps, lr.FLAG_SEPARATE_SHRINK)
+    shrink_us_step = (sprof["shrink"]["ms"] + sprof["sgmv_shrink"]["ms"]) * 1e3 / prof_steps
+    shrink_gbs = shrink_bytes / (shrink_us_step * 1e-6) / 1e9
+    separate = {
+        "flags": "LORA_FLAG_SEPARATE_SHRINK",
+        "ms_per_step": round(sep_ms, 4),
+        "tokens_per_s": M / (sep_ms * 1e-3),
+        "per_launch_us": {k_: round(sprof[k_]["ms"] * 1e3 / sprof[k_]["launches"], 3)
+                          for k_ in lr.KERNEL_CLASSES if sprof[k_]["launches"]},
+    }
+    log("separate shrink: %.3f ms/step, per-launch us %s" % (sep_ms, json.dumps(separate["per_launch_us"])))
 
     traffic = None
     try:
@@ -225,7 +256,9 @@ def main():
             "buffer_set_mb": round(set_bytes / 1e6, 1),
         },
         "roofline": {
-            "kernel": "k_gemm_bf16_pipe (base GEMM over the stacked q+v weight)",
+            "kernel": ("k_gemm_bf16_pipe (base GEMM over the stacked q+v weight, shrink folded in; "
+                       "achieved counts the base GEMM's and the shrink's algorithmic flops)"
+                       if folded else "k_gemm_bf16_pipe (base GEMM over the stacked q+v weight)"),
             "bound": "mfma",
             "achieved": gemm_tflops,
             "peak": BF16_PEAK_TFLOPS,
@@ -240,8 +273,11 @@ def main():
             "event_pass_ms_per_step": round(ev_elapsed * 1e3 / prof_steps, 4),
             "tokens_per_s_from_kernel_sum": M / (kernel_us_step * 1e-6),
             "gemm_tflops": round(gemm_tflops, 1),
+            "shrink_folded_into_gemm": folded,
             "shrink_gbs": round(shrink_gbs, 1),
             "shrink_frac_hbm": round(shrink_gbs / HBM_PEAK_GBS, 4),
+            "shrink_measured_in": "separate-shrink pass (the shrink kernel alone)",
+            "separate_shrink_step": separate,
             "expand_gbs": round(expand_gbs, 1),
             "expand_frac_hbm": round(expand_gbs / HBM_PEAK_GBS, 4),
             "algorithmic": {"q": bq, "v": bv, "fused_shrink_bytes": shrink_bytes},

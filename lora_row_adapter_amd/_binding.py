@@ -19,6 +19,7 @@ _LIB_NAME = "liblora_row.so"
 
 PATH_AUTO, PATH_GATHER, PATH_SGMV = 0, 1, 2
 FLAG_REUSE_PLAN = 1
+FLAG_SEPARATE_SHRINK = 2
 KIND_SLOTS, KIND_POOL = 0, 1
 PLAN_MAX_ROWS = 8192
 KERNEL_CLASSES = ("plan", "gemm", "shrink", "expand", "sgmv_shrink", "sgmv_expand")

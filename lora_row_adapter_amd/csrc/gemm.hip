@@ -166,6 +166,7 @@ struct PipeArgs {
   int64_t ldy;
   int tiles_m, tiles_n;
   int vec_store;  // y rows 16-byte aligned (ldy % 8 == 0, aligned base)
+  FusedT ft;      // TX kernels only
 };
 
 template <int N>
@@ -187,7 +188,21 @@ __device__ __forceinline__ void load16_to_lds(const void *base, uint32_t nbytes,
                                            voff, 0, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool PC>
+// TX: the shrink rides along (FusedT).  The 16 padding rows of the W stage
+// (BN = 144 is not a multiple of the 32-row load pattern) carry this column
+// tile's 16 stacked A rows, loaded by the producer that owns them from
+// per-lane addresses; the consumers run one more 16-column MFMA block and
+// scatter its fp32 results into t after the k loop.  Where the ranks sum
+// past the launch's capacity, the consumers then compute this tile's second
+// set of 16 columns with operands straight from global memory (a fallback:
+// x is read again).
+// The same from a per-lane global address (no bounds: the caller keeps
+// every lane's 16 bytes inside a live buffer).
+__device__ __forceinline__ void load16_to_lds_at(const uint8_t *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool PC, bool TX>
 __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
   constexpr int BKB = 128;                               // bytes per tile row (64 bf16)
   constexpr int BROWS = ((BN + 31) / 32) * 32;           // B rows loaded (multiple of 32)
@@ -197,13 +212,18 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
   constexpr int A_BYTES = BM * BKB;
   constexpr int STAGE_BYTES = (BM + BROWS) * BKB;
   constexpr int FM = BM / WM / 16;
-  constexpr int FN = BN / WN / 16;
+  constexpr int FN = BN / WN / 16 + (TX ? 1 : 0);        // TX: + the t block
+  constexpr int FNY = BN / WN / 16;                      // blocks that go to y
   constexpr int CLD = BN + 8;                            // epilogue LDS row (bf16)
   static_assert(WM * WN == 4, "4 waves");
-  static_assert(FM * WM * 16 == BM && FN * WN * 16 == BN, "tile split");
+  static_assert(FM * WM * 16 == BM && FNY * WN * 16 == BN, "tile split");
+  static_assert(!TX || (PC && WN == 1 && BROWS - BN == 16), "t rows fill the W stage's padding");
   constexpr int ECH = (STAGES * STAGE_BYTES >= BM * CLD * 2) ? BM : BM / 2;  // epilogue rows per pass
   static_assert(STAGES * STAGE_BYTES >= ECH * CLD * 2, "epilogue fits");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  // TX: t column c of this tile's pass p -> (slice << 16 | adapter << 8 |
+  // rank) or -1 at [16 p + c]; [32]: the clamped rank sum
+  __shared__ int32_t tmap[TX ? 33 : 1];
 
   const int b = blockIdx.x;
   const int nblk = p.tiles_m * p.tiles_n;
@@ -215,7 +235,7 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const bool producer = PC && wave >= 4;
   const int pw = wave & 3;  // index among the producers / among the consumers
 
@@ -243,18 +263,91 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
     vb[i] = row < BN ? (uint32_t)(row * p.ldw * 2 + c * 16) : 0xFFFFFFF0u;
   }
 
+  // TX: the producer whose load pattern covers the padding rows builds the
+  // column map (a wave-wide scan of the clamped ranks in (slice, adapter)
+  // order) and the per-lane source rows of its padding-row loads; unused
+  // columns read this tile's first x row instead (their results are dropped).
+  // It issues the rest of its prologue loads first, so the ranks' latency
+  // does not hold up the first tiles.
+  constexpr int TP = (BN / 8) / B_INSTR;                // that producer
+  constexpr int TE = TX ? (TP + 1) * B_INSTR - BN / 8 : 0;  // its padding-row loads per tile
+  static_assert(!TX || (TP + 1) * B_INSTR * 8 == BROWS, "padding rows within one producer");
+  const bool t_loader = TX && producer && pw == TP;
+  const uint8_t *tsrc[B_INSTR];
+  auto build_map = [&] {
+    if constexpr (TX) {
+      const FusedT &ft = p.ft;
+      const int nent = ft.n_slices * ft.S;
+      int rl[4], q4[4], a4[4], loc = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = lane * 4 + u;
+        const int q = f / max(ft.S, 1);
+        q4[u] = q;
+        a4[u] = f - q * ft.S;
+        // unconditional loads at a clamped entry, masked afterwards
+        const int fc = min(f, nent - 1);
+        const int qc = fc / max(ft.S, 1);
+        const int r = min(max(ft.ranks[qc][fc - qc * ft.S], 0), ft.R[qc]);
+        rl[u] = f < nent ? r : 0;
+        loc += rl[u];
+      }
+      int inc = loc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+      }
+      const int total = __shfl(inc, 63, 64);
+      if (lane < 32) tmap[lane] = -1;
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int e0 = pass * ft.cap + 16 * tn;
+        int start = inc - loc;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          for (int e = max(start, e0); e < min(start + rl[u], e0 + 16); ++e)
+            tmap[16 * pass + e - e0] = (q4[u] << 16) | (a4[u] << 8) | (e - start);
+          start += rl[u];
+        }
+      }
+      if (lane == 0) tmap[32] = total;
+#pragma unroll
+      for (int i = 0; i < B_INSTR; ++i) {
+        const int P = (pw * B_INSTR + i) * 64 + lane;
+        const int row = P >> 3;
+        const int c = (P & 7) ^ (row & 7);
+        const int v = row >= BN ? tmap[row - BN] : -1;
+        if (v >= 0) {
+          const int q = v >> 16, a = (v >> 8) & 255, j = v & 255;
+          tsrc[i] = ft.A[q] + (((int64_t)a * ft.R[q] + j) * p.K) * 2 + c * 16;
+        } else {
+          tsrc[i] = reinterpret_cast<const uint8_t *>(xa) + c * 16;
+        }
+      }
+    }
+  };
+
   const int nk = p.K / 64;
-  auto issue = [&](int kt, int stage) {
+  // part: 0 every load of the tile, 1 all but the padding rows, 2 those only
+  auto issue = [&](int kt, int stage, int part = 0) {
     uint8_t *sa = smem + stage * STAGE_BYTES;
     uint8_t *sb = sa + A_BYTES;
     const uint32_t kb = (uint32_t)kt * BKB;
+    if (part != 2) {
 #pragma unroll
-    for (int i = 0; i < A_INSTR; ++i)
-      load16_to_lds(xa, a_bytes, sa + (pw * A_INSTR + i) * 1024, va[i] + kb);
+      for (int i = 0; i < A_INSTR; ++i)
+        load16_to_lds(xa, a_bytes, sa + (pw * A_INSTR + i) * 1024, va[i] + kb);
+    }
 #pragma unroll
-    for (int i = 0; i < B_INSTR; ++i)
-      load16_to_lds(wb, b_bytes, sb + (pw * B_INSTR + i) * 1024,
-                    vb[i] == 0xFFFFFFF0u ? vb[i] : vb[i] + kb);
+    for (int i = 0; i < B_INSTR; ++i) {
+      if (TX && t_loader && (pw * B_INSTR + i) * 8 >= BN) {
+        if (part != 1) load16_to_lds_at(tsrc[i] + kb, sb + (pw * B_INSTR + i) * 1024);
+      } else if (part != 2) {
+        load16_to_lds(wb, b_bytes, sb + (pw * B_INSTR + i) * 1024,
+                      vb[i] == 0xFFFFFFF0u ? vb[i] : vb[i] + kb);
+      }
+    }
   };
 
   f32x4_t acc[FM][FN];
@@ -264,7 +357,7 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int wm0 = (pw / WN) * (FM * 16);
-  const int wn0 = (pw % WN) * (FN * 16);
+  const int wn0 = (pw % WN) * (FNY * 16);
 
   auto compute = [&](int kt) {
     const uint8_t *sa = smem + (kt % STAGES) * STAGE_BYTES;
@@ -287,6 +380,22 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
     }
   };
   auto wait_tile = [&](int kt) {
+    if (t_loader && kt < STAGES - 2) {
+      // its prologue issued the padding rows of tiles 0..STAGES-2 after the
+      // rest: what may still be in flight once tile kt has landed
+      static_assert(!TX || STAGES == 3 || STAGES == 4, "prologue orders for 2 or 3 tiles ahead");
+      if (STAGES == 3) {
+        if (nk >= 2) wait_vmcnt<TE>();
+        else wait_vmcnt<0>();
+      } else if (kt == 0) {
+        if (nk >= 3) wait_vmcnt<2 * TE>();
+        else wait_vmcnt<0>();
+      } else {
+        if (nk >= 4) wait_vmcnt<TE + LOADS>();
+        else wait_vmcnt<0>();
+      }
+      return;
+    }
     const int rem = min(STAGES - 2, nk - 1 - kt);
     if (rem >= 2) wait_vmcnt<2 * LOADS>();
     else if (rem == 1) wait_vmcnt<LOADS>();
@@ -303,7 +412,15 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
     asm volatile("" ::: "memory");
   };
 
-  if (!PC || producer) {
+  if (t_loader) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(s, s, 1);
+    build_map();
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(s, s, 2);
+  } else if (!PC || producer) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < nk) issue(s, s);
@@ -328,6 +445,74 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
     }
   }
 
+  if constexpr (TX) {
+    // t: this tile's rows x its 16 t columns, kept where the row's adapter
+    // owns the column (tmap was written before the k loop's barriers)
+    if (!producer) {
+      const FusedT &ft = p.ft;
+      // the rows' ids first (one batch of loads at clamped rows)
+      int id[FM][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          id[i][e] = ft.ids[min(m0 + wm0 + i * 16 + ((lane >> 4) << 2) + e, p.M - 1)];
+      auto scatter = [&](int v, const f32x4_t (&t)[FM]) {
+        if (v < 0) return;
+        const int q = v >> 16, a = (v >> 8) & 255, j = v & 255;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = m0 + wm0 + i * 16 + ((lane >> 4) << 2) + e;
+            if (m < p.M && id[i][e] == a)
+              ft.tpart[((int64_t)m * ft.n_slices + q) * ft.Rw + j] = t[i][e];
+          }
+      };
+      f32x4_t t0[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) t0[i] = acc[i][FN - 1];
+      scatter(tmap[lane & 15], t0);
+      if (tmap[32] > ft.cap) {  // uniform
+        // second pass: MFMA operands straight from global memory (x rows in
+        // the A-operand layout, the column's A row in the B-operand layout),
+        // loads at clamped rows / a valid dummy row, all issued before use
+        const int v1 = tmap[16 + (lane & 15)];
+        const int kl = (lane >> 4) * 8;
+        const uint16_t *asrc;
+        if (v1 >= 0) {
+          const int q = v1 >> 16, a = (v1 >> 8) & 255, j = v1 & 255;
+          asrc = reinterpret_cast<const uint16_t *>(ft.A[q]) + ((int64_t)a * ft.R[q] + j) * p.K + kl;
+        } else {
+          asrc = p.x + (int64_t)m0 * p.ldx + kl;
+        }
+        const uint16_t *xr[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          xr[i] = p.x + (int64_t)min(m0 + wm0 + i * 16 + (lane & 15), p.M - 1) * p.ldx + kl;
+        f32x4_t t1[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) t1[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < p.K; k0 += 64) {  // K % 64 == 0
+          bf16x8_t xf[2][FM], af[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+              xf[u][i] = *reinterpret_cast<const bf16x8_t *>(xr[i] + k0 + 32 * u);
+            af[u] = *reinterpret_cast<const bf16x8_t *>(asrc + k0 + 32 * u);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+              t1[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][i], af[u], t1[i], 0, 0, 0);
+        }
+        scatter(v1, t1);
+      }
+    }
+  }
+
   // epilogue: bf16 tile through LDS (ECH rows per pass), then 16-byte row stores
   constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
   uint16_t *ct = reinterpret_cast<uint16_t *>(smem);
@@ -339,7 +524,7 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
       const int rb = wm0 + i * 16;
       if (producer || rb < r0 || rb >= r0 + ECH) continue;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FNY; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           ct[(rb - r0 + ((lane >> 4) << 2) + e) * CLD + wn0 + j * 16 + (lane & 15)] =
@@ -415,7 +600,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int M, int N, int K, const flo
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, bool TX = false>
 void launch_pipe(const PipeArgs &pa0, hipStream_t st) {
   PipeArgs pa = pa0;
   pa.tiles_m = (pa.M + BM - 1) / BM;
@@ -423,8 +608,53 @@ void launch_pipe(const PipeArgs &pa0, hipStream_t st) {
   // separate producer waves where the consumers' accumulators leave room
   // for a second wave per SIMD (at most 128 fp32 per lane)
   constexpr bool PC = (BM / WM) * (BN / WN) / 64 <= 128;
-  hipLaunchKernelGGL((k_gemm_bf16_pipe<BM, BN, WM, WN, STAGES, PC>), dim3(pa.tiles_m * pa.tiles_n),
-                     dim3(PC ? 512 : 256), 0, st, pa);
+  hipLaunchKernelGGL((k_gemm_bf16_pipe<BM, BN, WM, WN, STAGES, PC, TX>),
+                     dim3(pa.tiles_m * pa.tiles_n), dim3(PC ? 512 : 256), 0, st, pa);
+}
+
+bool pipe_ok(int64_t k, int64_t ldx, int64_t ldw) {
+  return (k % 64) == 0 && (uint64_t)256 * ldx * 2 < (1ull << 32) &&
+         (uint64_t)256 * ldw * 2 < (1ull << 32);
+}
+
+// Tile choice: fill the 256 CUs with as few, as large tiles as possible.
+// Relative per-FLOP costs of the shapes were measured on MI355X (bigger
+// tiles move fewer bytes per FLOP into LDS).  Returns the index into the
+// launch switch below.
+int choose_tile(int64_t M, int64_t d) {
+  struct Cand { int bm, bn; double cost; };
+  const Cand cands[] = {{256, 256, 0.87}, {256, 128, 0.90}, {128, 144, 0.97},
+                        {128, 128, 1.00}, {64, 64, 2.2}};
+  int best = 3;
+  double best_t = 1e30;
+  for (int c = 0; c < 5; ++c) {
+    const Cand &cd = cands[c];
+    if (cd.bn == 144 && d % 144 != 0) continue;
+    const int64_t tiles = ((M + cd.bm - 1) / cd.bm) * ((d + cd.bn - 1) / cd.bn);
+    const int64_t rounds = (tiles + 255) / 256;
+    const double t_est = (double)rounds * cd.bm * cd.bn * cd.cost;
+    if (t_est < best_t * 0.999) {
+      best_t = t_est;
+      best = c;
+    }
+  }
+  return best;
+}
+
+PipeArgs pipe_args(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx, const void *W,
+                   int64_t ldw, void *y, int64_t ldy) {
+  PipeArgs pa{};
+  pa.M = (int)M;
+  pa.N = (int)d;
+  pa.K = (int)k;
+  pa.x = (const uint16_t *)x;
+  pa.ldx = ldx;
+  pa.W = (const uint16_t *)W;
+  pa.ldw = ldw;
+  pa.y = (uint16_t *)y;
+  pa.ldy = ldy;
+  pa.vec_store = ((ldy % 8) == 0 && ((uintptr_t)y & 15) == 0) ? 1 : 0;
+  return pa;
 }
 
 }  // namespace
@@ -433,43 +663,12 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
                        const void *W, int64_t ldw, void *y, int64_t ldy, hipStream_t st) {
   if (M <= 0 || d <= 0) return hipSuccess;
   if (dtype == 1) {
-    const bool pipe_ok = (k % 64) == 0 && (uint64_t)256 * ldx * 2 < (1ull << 32) &&
-                         (uint64_t)256 * ldw * 2 < (1ull << 32);
-    if (pipe_ok) {
-      PipeArgs pa{};
-      pa.M = (int)M;
-      pa.N = (int)d;
-      pa.K = (int)k;
-      pa.x = (const uint16_t *)x;
-      pa.ldx = ldx;
-      pa.W = (const uint16_t *)W;
-      pa.ldw = ldw;
-      pa.y = (uint16_t *)y;
-      pa.ldy = ldy;
-      pa.vec_store = ((ldy % 8) == 0 && ((uintptr_t)y & 15) == 0) ? 1 : 0;
-      // Tile choice: fill the 256 CUs with as few, as large tiles as
-      // possible.  Relative per-FLOP costs of the shapes were measured on
-      // MI355X (bigger tiles move fewer bytes per FLOP into LDS).
-      struct Cand { int bm, bn; double cost; };
-      const Cand cands[] = {{256, 256, 0.87}, {256, 128, 0.90}, {128, 144, 0.97},
-                            {128, 128, 1.00}, {64, 64, 2.2}};
-      int best = 3;
-      double best_t = 1e30;
-      for (int c = 0; c < 5; ++c) {
-        const Cand &cd = cands[c];
-        if (cd.bn == 144 && d % 144 != 0) continue;
-        const int64_t tiles = ((M + cd.bm - 1) / cd.bm) * ((d + cd.bn - 1) / cd.bn);
-        const int64_t rounds = (tiles + 255) / 256;
-        const double t_est = (double)rounds * cd.bm * cd.bn * cd.cost;
-        if (t_est < best_t * 0.999) {
-          best_t = t_est;
-          best = c;
-        }
-      }
-      switch (best) {
+    if (pipe_ok(k, ldx, ldw)) {
+      const PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
+      switch (choose_tile(M, d)) {
         case 0: launch_pipe<256, 256, 2, 2, 2>(pa, st); break;
         case 1: launch_pipe<256, 128, 4, 1, 3>(pa, st); break;
-        case 2: launch_pipe<128, 144, 4, 1, 4>(pa, st); break;
+        case 2: launch_pipe<128, 144, 4, 1, 3>(pa, st); break;
         case 3: launch_pipe<128, 128, 2, 2, 4>(pa, st); break;
         default: launch_pipe<64, 64, 2, 2, 4>(pa, st); break;
       }
@@ -486,6 +685,23 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
     hipLaunchKernelGGL(k_gemm_f32, dim3(tiles_m * tiles_n), dim3(256), 0, st, (int)M, (int)d,
                        (int)k, (const float *)x, ldx, (const float *)W, ldw, (float *)y, ldy);
   }
+  return hipGetLastError();
+}
+
+int32_t gemm_fused_cap(int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw) {
+  if (M <= 0 || d <= 0 || !pipe_ok(k, ldx, ldw) || choose_tile(M, d) != 2) return 0;
+  return (int32_t)(16 * ((d + 143) / 144));
+}
+
+hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
+                             const void *W, int64_t ldw, void *y, int64_t ldy, const FusedT &ft,
+                             hipStream_t st) {
+  if (ft.cap <= 0 || ft.cap != gemm_fused_cap(M, k, d, ldx, ldw) ||
+      ft.n_slices * ft.S > kFusedMaxEntries || ft.S > 256 || ft.n_slices > kMaxSlices)
+    return hipErrorInvalidValue;
+  PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
+  pa.ft = ft;
+  launch_pipe<128, 144, 4, 1, 3, true>(pa, st);
   return hipGetLastError();
 }
 

@@ -61,15 +61,46 @@ struct LoraArgs {
   WsLayout L;
   int32_t ksplit;
   int64_t kchunk;  // k per split (multiple of 256)
+  // > 0: this call's base GEMM computed t into split 0 of the partials,
+  // indexed by row (no shrink launch); the expand reads that t
+  int32_t fused_cap;
 };
 
 hipError_t launch_plan(const PlanArgs &a, hipStream_t st);
 hipError_t launch_translate(const AdapterRef &ar, int32_t S, int64_t n_pages,
                             const int32_t *adapter, const int64_t *off, int64_t n,
                             int64_t *phys, hipStream_t st);
+// The shrink folded into the base GEMM (bf16, adapters in slots).  The
+// (slice, adapter, rank) triples with rank < that adapter's rank (clamped
+// to [0, max_rank]), in that order, form the columns of t_all = x A_cat^T;
+// column tile tn of the GEMM computes columns [16 tn, 16 tn + 16) of t_all
+// from 16 extra rows of its W stage, and columns [cap + 16 tn, + 16) -- if
+// the ranks sum past cap -- in a second pass after its k loop; it writes
+// t[slice][row][rank] (split 0 of the partials layout, indexed by the row
+// itself) for the rows whose adapter owns the column.  The caller keeps
+// n_slices * S * max_rank <= 2 * cap.
+struct FusedT {
+  int32_t cap;     // 16 x column tiles of the launch; 0: not fused
+  int32_t n_slices, S;
+  const uint8_t *A[kMaxSlices];   // slot A [S][R][k] of each slice
+  int32_t R[kMaxSlices];          // max_rank of each slice (rank stride of A)
+  const int32_t *ranks[kMaxSlices];
+  const int32_t *ids;             // adapter id of each row
+  float *tpart;                   // partials region of the workspace
+  int64_t rows;                   // its row stride (WsLayout::rows)
+  int32_t Rw;                     // its row width (WsLayout::R)
+};
+constexpr int kFusedMaxEntries = 256;  // n_slices * S the fused path scans
 // Base GEMM y = x W^T (bf16 operands: MFMA tiles; fp32: VALU).
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, hipStream_t st);
+// Capacity (t_all columns) a fused launch of this shape would have; 0 when
+// the shape's tile cannot carry the extra rows.
+int32_t gemm_fused_cap(int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw);
+// The base GEMM with the shrink folded in (ft.cap == gemm_fused_cap(...)).
+hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
+                             const void *W, int64_t ldw, void *y, int64_t ldy, const FusedT &ft,
+                             hipStream_t st);
 // Base GEMM with a quantized weight (bf16 x and y).
 struct QGemmArgs {
   int32_t fmt;  // 1 INT8 (per-row scales), 2 INT4 (per-row, per-k-group scales)

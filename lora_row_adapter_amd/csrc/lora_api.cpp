@@ -453,7 +453,7 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
          : check_gemm_args(dtype, M, k, d_total, x, ldx, W, ldw, y, ldy);
   if (s != LORA_OK) return s;
   if (path != LORA_PATH_AUTO && path != LORA_PATH_GATHER && path != LORA_PATH_SGMV) return LORA_ERR_ARG;
-  if ((flags & ~LORA_FLAG_REUSE_PLAN) != 0) return LORA_ERR_ARG;
+  if ((flags & ~(LORA_FLAG_REUSE_PLAN | LORA_FLAG_SEPARATE_SHRINK)) != 0) return LORA_ERR_ARG;
   if (M == 0) return LORA_OK;
   if (adapter_ids == nullptr || workspace == nullptr) return LORA_ERR_ARG;
   for (int q = 0; q < n_slices; ++q)
@@ -534,6 +534,39 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
     a.ksplit = (int32_t)ks;
     a.kchunk = kchunk;
 
+    // Folded shrink: the base GEMM carries the stacked A rows (slots only:
+    // each A row is one contiguous run) when its tile shape has room for
+    // every rank in at most two passes (the second is a fallback for rank
+    // sums past the first pass's capacity).
+    int32_t fcap = 0;
+    if (!qw && dtype == LORA_DTYPE_BF16 && use_mfma && !(flags & LORA_FLAG_SEPARATE_SHRINK) &&
+        (int64_t)n_slices * S <= kFusedMaxEntries && S <= 256) {
+      bool slots = true;
+      int64_t worst = 0;
+      for (int q = 0; q < n_slices; ++q) {
+        slots = slots && slices[q].adapters.kind == LORA_ADAPTERS_SLOTS &&
+                ((uintptr_t)slices[q].adapters.A & 15u) == 0;
+        worst += (int64_t)S * slices[q].adapters.max_rank;
+      }
+      const int32_t cap = slots ? gemm_fused_cap(Mc, k, d_total, ldx, ldw) : 0;
+      if (cap > 0 && worst <= 2 * (int64_t)cap) fcap = cap;
+    }
+    a.fused_cap = fcap;
+    FusedT ft{};
+    if (fcap > 0) {
+      ft.cap = fcap;
+      ft.n_slices = n_slices;
+      ft.S = S;
+      for (int q = 0; q < n_slices; ++q) {
+        ft.A[q] = (const uint8_t *)slices[q].adapters.A;
+        ft.R[q] = slices[q].adapters.max_rank;
+        ft.ranks[q] = slices[q].adapters.ranks;
+      }
+      ft.ids = adapter_ids + c0;
+      ft.tpart = (float *)(ws + L.tpart);
+      ft.rows = L.rows;
+      ft.Rw = L.R;
+    }
     // The plan needs only the ids, the GEMM only x and W: with a side
     // stream the plan runs beside the GEMM and the caller's stream waits
     // for it before the shrink.  (A shrink on the side stream as well gets
@@ -555,14 +588,17 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
     }
     hipError_t e = timed(LORA_K_GEMM, st, [&] {
       if (qw) return launch_gemm_q(make_q_args(qw, Mc, k, d_total, xc, ldx, yc, ldy), st);
+      if (fcap > 0) return launch_gemm_fused(Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, ft, st);
       return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, st);
     });
     if (e != hipSuccess) return LORA_ERR_HIP;
     if (fork && hipStreamWaitEvent(st, ev_join, 0) != hipSuccess) return LORA_ERR_HIP;
 
     if (use_mfma) {
-      e = timed(LORA_K_SGMV_SHRINK, st, [&] { return launch_shrink_sgmv(a, rpi, per_slice, st); });
-      if (e != hipSuccess) return LORA_ERR_HIP;
+      if (fcap == 0) {  // else the base GEMM computed t
+        e = timed(LORA_K_SGMV_SHRINK, st, [&] { return launch_shrink_sgmv(a, rpi, per_slice, st); });
+        if (e != hipSuccess) return LORA_ERR_HIP;
+      }
       e = timed(LORA_K_SGMV_EXPAND, st, [&] { return launch_expand_sgmv(a, rpi, st); });
       if (e != hipSuccess) return LORA_ERR_HIP;
     } else {

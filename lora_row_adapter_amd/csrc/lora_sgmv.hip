@@ -448,7 +448,11 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
     }
   }
 
-  // 2. t = sum of the k-split partials, as bf16 hi + lo (4 ranks per thread)
+  // 2. t = sum of the k-split partials, as bf16 hi + lo (4 ranks per thread);
+  //    where the base GEMM computed t (one split, indexed by the row itself)
+  //    it is read from there
+  const bool t_by_row = a.fused_cap > 0;
+  const int nsplit = t_by_row ? 1 : a.ksplit;
   const int kp4 = kp >> 2;
   for (int e = tid; e < RB * kp4; e += 256) {
     const int row = e / kp4;
@@ -456,15 +460,17 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (FAST) {
       const bool ok = row < nr && j < r;
-      v = tpart_sum4(tpart, it.pos + (ok ? row : 0), slice, ok ? j : 0, a.ksplit, a.L.rows,
-                     a.n_slices, a.L.R);
+      const int rc = ok ? row : 0;
+      const int64_t tp = t_by_row ? (int64_t)item_row<RB == 16>(ix, perm, it, rc) : it.pos + rc;
+      v = tpart_sum4(tpart, tp, slice, ok ? j : 0, nsplit, a.L.rows, a.n_slices, a.L.R);
       // entries past the rank are never written by the shrink
       v.x = ok ? v.x : 0.f;
       v.y = ok && j + 1 < r ? v.y : 0.f;
       v.z = ok && j + 2 < r ? v.z : 0.f;
       v.w = ok && j + 3 < r ? v.w : 0.f;
     } else if (row < nr && j < r) {
-      v = tpart_sum4(tpart, it.pos + row, slice, j, a.ksplit, a.L.rows, a.n_slices, a.L.R);
+      const int64_t tp = t_by_row ? (int64_t)item_row<RB == 16>(ix, perm, it, row) : it.pos + row;
+      v = tpart_sum4(tpart, tp, slice, j, nsplit, a.L.rows, a.n_slices, a.L.R);
       // entries past the rank are never written by the shrink
       if (j + 1 >= r) v.y = 0.f;
       if (j + 2 >= r) v.z = 0.f;

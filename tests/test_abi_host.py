@@ -95,7 +95,7 @@ def test_linear_rejects_bad_arguments_on_host():
     assert _linear(lib, c, ws=8200) == 5                  # workspace misaligned
     assert _linear(lib, c, ws_bytes=100) == 5             # workspace too small
     assert _linear(lib, c, path=9) == 1                   # bad path
-    assert _linear(lib, c, flags=2) == 1                  # unknown flag
+    assert _linear(lib, c, flags=4) == 1                  # unknown flag
     assert _linear(lib, c, M=9000, flags=1) == 1          # plan reuse across row chunks
     assert _linear(lib, c, M=-1) == 2
     assert _linear(lib, c, M=0) == 0                      # empty batch is a no-op

@@ -1,0 +1,161 @@
+"""The shrink folded into the base GEMM, on the GPU, through the C ABI.
+
+Where the base GEMM runs 128 x 144 tiles (bf16, adapters in slots), each
+column tile also computes 16 columns of t = x A^T over the stacked
+(slice, adapter, rank) list -- and 16 more in a second pass where the ranks
+sum past the first pass's capacity -- and no shrink is launched.  Checked
+against the fp64 oracle (normwise 2e-2, the layer's bf16 bound), against the
+same call with LORA_FLAG_SEPARATE_SHRINK (t summed in another order: the two
+outputs differ by bf16 rounding of y only), and through the library's own
+launch counters (which kernels ran).  Shapes: 400 rows (three full 128-row
+tiles and a 16-row tail) and sum d = 9216, the range where 128 x 144 tiles
+are chosen; k = 512 keeps the oracle fast.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lora_row_adapter_amd as lr
+from lora_row_adapter_amd import workloads as wl
+from gpu_helpers import DevWorkload, normwise, oracle_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    torch.cuda.set_device(0)
+    lr.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def launches(fn):
+    """Run fn under the library's launch counters; kernel class -> launches."""
+    with lr.Profiler():
+        fn()
+        torch.cuda.synchronize()
+        prof = lr.Profiler.read(reset=True)
+    return {k: prof[k]["launches"] for k in lr.KERNEL_CLASSES}
+
+
+def sliced_pair(w):
+    """Device slices for a two-projection workload (q then v)."""
+    dev = torch.device("cuda")
+    ranks = torch.from_numpy(w.ranks).to(dev)
+    scales = torch.from_numpy(w.scales).to(dev)
+    slices, keep = [], []
+    for p in (w.proj("q"), w.proj("v")):
+        A, B = wl.slots(w, p)
+        A, B = A.to(dev), B.to(dev)
+        keep.append((A, B))
+        slices.append(lr.Slice(p.d, lr.Adapters.slots(A, B, ranks), scales))
+    W = torch.cat([w.proj("q").W, w.proj("v").W], dim=0).contiguous().to(dev)
+    return W, slices, keep
+
+
+def test_two_slices_fused_matches_oracle(oracle_mod):
+    """q + v slices with the 70B adapter set (ranks 4/16/64, sum 600 of a
+    1024-column first pass)."""
+    w = wl.c3_proj70b_bf16(M=400, k=512, d_q=8064, d_v=1152)
+    W, slices, _keep = sliced_pair(w)
+    x, ids = w.x.cuda(), torch.from_numpy(w.ids).cuda()
+    out = {}
+    for name, flags in (("fused", 0), ("separate", lr.FLAG_SEPARATE_SHRINK)):
+        say("two slices, %s shrink" % name)
+        res = {}
+        cnt = launches(lambda: res.setdefault("y", lr.lora_linear_sliced(x, W, slices, ids, flags=flags)))
+        out[name] = res["y"]
+        assert cnt["gemm"] == 1 and cnt["sgmv_expand"] == 1, cnt
+        assert cnt["sgmv_shrink"] == (0 if flags == 0 else 1), cnt
+    for name, y in out.items():
+        for p, lo in ((w.proj("q"), 0), (w.proj("v"), 8064)):
+            ref = oracle_rows(oracle_mod, w, p)
+            err = normwise(y[:, lo:lo + p.d].double().cpu().numpy(), ref)
+            say("  %s %s normwise %.3g" % (name, p.name, err))
+            assert err <= 2e-2
+    # t summed in another order: y may differ in the last bf16 place only
+    diff = normwise(out["fused"].double().cpu().numpy(), out["separate"].double().cpu().numpy())
+    say("  fused vs separate normwise %.3g" % diff)
+    assert diff <= 1e-2
+    # rows without an adapter are the base GEMM bit for bit
+    base = lr.lora_gemm(x, W)
+    none = torch.from_numpy(np.flatnonzero(w.ids < 0)).cuda()
+    assert torch.equal(out["fused"][none], base[none])
+
+
+def test_small_adapter_set_one_pass(oracle_mod):
+    """8 adapters x max_rank 64 = 512 <= 1024: one pass, no shrink launch."""
+    w = wl.custom(seed=21, M=400, k=512, d=9216, ranks=[16, 64, 8, 0, 33, 64, 1, 16], max_rank=64,
+                  none_frac=0.1)
+    p = w.projections[0]
+    dw = DevWorkload(w, p)
+    res = {}
+    cnt = launches(lambda: res.setdefault("y", dw.run()))
+    assert cnt["sgmv_shrink"] == 0 and cnt["gemm"] == 1 and cnt["sgmv_expand"] == 1, cnt
+    err = normwise(res["y"].double().cpu().numpy(), oracle_rows(oracle_mod, w, p))
+    say("no-shrink fused normwise %.3g" % err)
+    assert err <= 2e-2
+    ysep = dw.run(flags=lr.FLAG_SEPARATE_SHRINK)
+    assert normwise(res["y"].double().cpu().numpy(), ysep.double().cpu().numpy()) <= 1e-2
+
+
+def test_ranks_past_first_pass_use_the_second(oracle_mod):
+    """20 adapters of rank 64 (sum 1280 > 1024): columns 1024.. come from
+    the GEMM's second pass; still no shrink launch."""
+    w = wl.custom(seed=22, M=400, k=512, d=9216, ranks=[64] * 20, max_rank=64, none_frac=0.05)
+    p = w.projections[0]
+    dw = DevWorkload(w, p)
+    res = {}
+    cnt = launches(lambda: res.setdefault("y", dw.run()))
+    assert cnt["sgmv_shrink"] == 0, cnt
+    y = res["y"]
+    err = normwise(y.double().cpu().numpy(), oracle_rows(oracle_mod, w, p))
+    say("second pass normwise %.3g" % err)
+    assert err <= 2e-2
+    ysep = dw.run(flags=lr.FLAG_SEPARATE_SHRINK)
+    assert normwise(y.double().cpu().numpy(), ysep.double().cpu().numpy()) <= 1e-2
+
+
+def test_too_many_ranks_are_not_folded(oracle_mod):
+    """40 adapters x max_rank 64 = 2560 > two passes of 1024: the shrink runs
+    as its own kernel."""
+    w = wl.custom(seed=25, M=400, k=256, d=9216, ranks=[64, 8] * 20, max_rank=64)
+    p = w.projections[0]
+    dw = DevWorkload(w, p)
+    res = {}
+    cnt = launches(lambda: res.setdefault("y", dw.run()))
+    assert cnt["sgmv_shrink"] == 1, cnt
+    err = normwise(res["y"].double().cpu().numpy(), oracle_rows(oracle_mod, w, p))
+    assert err <= 2e-2
+
+
+def test_out_of_range_ranks_are_clamped_and_ignored(oracle_mod):
+    """A rank above max_rank or below zero: the fold clamps it (no read past
+    the slot) and the plan turns that adapter's rows into base rows.  With
+    rank 64 clamped in, the sum (16 + 64 + 0 + 32) stays in one pass."""
+    w = wl.custom(seed=23, M=400, k=512, d=9216, ranks=[16, 64, 8, 32], max_rank=64)
+    p = w.projections[0]
+    dw = DevWorkload(w, p)
+    dw.ranks[1] = 1000
+    dw.ranks[2] = -3
+    y = dw.run()
+    ids = w.ids.copy()
+    ids[np.isin(ids, [1, 2])] = -1
+    err = normwise(y.double().cpu().numpy(), oracle_rows(oracle_mod, w, p, ids=ids))
+    say("clamped ranks normwise %.3g" % err)
+    assert err <= 2e-2
+    base = lr.lora_gemm(dw.x, dw.W)
+    bad = torch.from_numpy(np.flatnonzero(np.isin(w.ids, [1, 2]))).cuda()
+    assert torch.equal(y[bad], base[bad])
+
+
+def test_reuse_plan_with_fold():
+    """A second call on the same ids with LORA_FLAG_REUSE_PLAN gives the same bits."""
+    w = wl.custom(seed=24, M=400, k=512, d=9216, ranks=[16, 64, 8, 0, 33, 64, 1, 16], max_rank=64)
+    dw = DevWorkload(w, w.projections[0])
+    y1 = dw.run()
+    y2 = dw.run(flags=lr.FLAG_REUSE_PLAN)
+    assert torch.equal(y1, y2)

@@ -245,9 +245,13 @@ def test_managed_pools_c3_sliced_match_slots(c3_workload):
     managed = [lr.Slice(pq.d, qpool.adapters(), dq.scales), lr.Slice(pv.d, vpool.adapters(), dv.scales)]
     stacked = [lr.Slice(pq.d, dq.ad, dq.scales), lr.Slice(pv.d, dv.ad, dv.scales)]
     y_m = lr.lora_linear_sliced(dq.x, W, managed, dq.ids)
-    y_s = lr.lora_linear_sliced(dq.x, W, stacked, dq.ids)
+    # the same kernels on the slots (the slot call would otherwise fold the
+    # shrink into the base GEMM, which sums t in another order)
+    y_s = lr.lora_linear_sliced(dq.x, W, stacked, dq.ids, flags=lr.FLAG_SEPARATE_SHRINK)
+    y_f = lr.lora_linear_sliced(dq.x, W, stacked, dq.ids)
     torch.cuda.synchronize()
     assert torch.equal(y_m, y_s)
+    assert normwise(y_f.double().cpu().numpy(), y_m.double().cpu().numpy()) <= 1e-2
 
 
 @pytest.fixture(scope="module")
