@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 
 typedef enum lora_status {
   LORA_OK = 0,
@@ -141,15 +141,30 @@ size_t lora_workspace_bytes(int64_t max_rows, int64_t d, int64_t k, lora_dtype_t
                             const lora_adapters_t *adapters);
 
 /*
- * Base projection only: y = x W^T.  Same kernels as the base step of
- * lora_linear, so rows with no adapter there are bitwise equal to this.
+ * Bytes of workspace lora_gemm uses for this shape: the fp32 partial tiles
+ * and arrival/ready words of its split-K workgroup pairs.  0 when the shape
+ * runs unsplit tiles (then lora_gemm needs no workspace).  Host-only.
+ */
+size_t lora_gemm_workspace_bytes(int64_t M, int64_t k, int64_t d, lora_dtype_t dtype);
+
+/*
+ * Base projection only: y = x W^T ("S-LoRA: what the paper actually says
+ * ...", section "Batched LoRA computation": the base term is one GEMM over
+ * the whole batch).  Same kernels as the base step of lora_linear: with a
+ * workspace of lora_gemm_workspace_bytes(M, k, d, dtype) bytes (or a
+ * lora_linear workspace for the same rows, whose GEMM region it is), rows
+ * with no adapter in lora_linear are bitwise equal to this.  Shapes that
+ * split k across workgroup pairs fall back to unsplit tiles when workspace
+ * is NULL or smaller (same values up to fp32 summation order).
  * x [M, k] (ldx >= k), W [d, k] (ldw >= k), y [M, d] (ldy >= d).
  * bf16: k, ldx, ldw multiples of 8 and ldy a multiple of 2; f32: k, ldx, ldw
- * multiples of 4.  M == 0 is a no-op.
+ * multiples of 4.  workspace: device, 256-byte aligned (else
+ * LORA_ERR_WORKSPACE), caller-owned, no initialisation needed; it must not
+ * be in use by another call that is still running.  M == 0 is a no-op.
  */
 lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
                         int64_t ldx, const void *W, int64_t ldw, void *y, int64_t ldy,
-                        void *stream);
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The LoRA linear layer (see the top of this file).

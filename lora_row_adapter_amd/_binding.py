@@ -137,8 +137,10 @@ def load_library():
     lib.lora_status_str.restype = ctypes.c_char_p
     lib.lora_workspace_bytes.argtypes = [i64, i64, i64, i32, pad]
     lib.lora_workspace_bytes.restype = sz
-    lib.lora_gemm.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.lora_gemm.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64, p, sz, p]
     lib.lora_gemm.restype = i32
+    lib.lora_gemm_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    lib.lora_gemm_workspace_bytes.restype = sz
     lib.lora_linear.argtypes = [i32, i64, i64, i64, p, i64, p, i64, pad, p, p, p, i64, p, sz, i32,
                                 u32, p]
     lib.lora_linear.restype = i32
@@ -489,9 +491,15 @@ def new_workspace(max_rows: int, d: int, k: int, dtype: torch.dtype, adapters: A
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
+def gemm_workspace_bytes(M: int, k: int, d: int, dtype: torch.dtype) -> int:
+    """Workspace bytes lora_gemm uses for this shape (0: none needed)."""
+    return int(load_library().lora_gemm_workspace_bytes(int(M), int(k), int(d), _DTYPES[dtype]))
+
+
 def lora_gemm(x: torch.Tensor, W: torch.Tensor, y: Optional[torch.Tensor] = None,
-              stream=None) -> torch.Tensor:
-    """y = x W^T on the device (base projection only)."""
+              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = x W^T on the device (base projection only).  Without a workspace
+    one of lora_gemm_workspace_bytes bytes is allocated (torch) for the call."""
     lib = load_library()
     if y is None:
         y = torch.empty((x.shape[0], W.shape[0]), dtype=x.dtype, device=x.device)
@@ -500,8 +508,13 @@ def lora_gemm(x: torch.Tensor, W: torch.Tensor, y: Optional[torch.Tensor] = None
     yp, ldy = _rows(y, "y")
     if W.dtype != x.dtype or y.dtype != x.dtype:
         raise TypeError("x, W, y must share a dtype")
+    if workspace is None:
+        n = gemm_workspace_bytes(x.shape[0], x.shape[1], W.shape[0], x.dtype)
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    wsp, wsn = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
     _check(lib.lora_gemm(_dtype_code(x), x.shape[0], x.shape[1], W.shape[0], xp, ldx, wp, ldw,
-                         yp, ldy, _stream_ptr(stream)), "lora_gemm")
+                         yp, ldy, wsp, wsn, _stream_ptr(stream)), "lora_gemm")
     return y
 
 

@@ -17,6 +17,8 @@
 // workgroups that share one W strip share that XCD's L2.
 //
 // fp32: plain VALU FMA tiles (64 x 64, 4 x 4 per thread); true fp32 products.
+#include <atomic>
+
 #include "kernels.hpp"
 
 namespace lora {
@@ -167,6 +169,11 @@ struct PipeArgs {
   int tiles_m, tiles_n;
   int vec_store;  // y rows 16-byte aligned (ldy % 8 == 0, aligned base)
   FusedT ft;      // TX kernels only
+  // split-K pairs (SK == 2): fp32 partial tiles, per pair an arrival word
+  // and a ready flag, and this launch's epoch
+  float *part;
+  uint64_t *sync;
+  uint64_t epoch;
 };
 
 template <int N>
@@ -202,8 +209,12 @@ __device__ __forceinline__ void load16_to_lds_at(const uint8_t *src, void *lds) 
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool PC, bool TX>
-__global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
+template <int BM, int BN, int WM, int WN, int STAGES, bool PC, bool TX, int SK>
+__device__ __forceinline__ void pipe_body(const PipeArgs &p) {
+  constexpr int NC = WM * WN;                            // MFMA (consumer) waves
+  constexpr int NT = PC ? 64 * NC + 256 : 256;           // threads
+  static_assert(NC == 4 || (NC == 8 && PC), "4 waves, or 8 beside separate producers");
+  static_assert(SK == 1 || (SK == 2 && PC), "split-K pairs use the producer layout");
   constexpr int BKB = 128;                               // bytes per tile row (64 bf16)
   constexpr int BROWS = ((BN + 31) / 32) * 32;           // B rows loaded (multiple of 32)
   constexpr int A_INSTR = BM * 8 / 256;                  // 16-byte loads per thread per k-tile
@@ -215,7 +226,6 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
   constexpr int FN = BN / WN / 16 + (TX ? 1 : 0);        // TX: + the t block
   constexpr int FNY = BN / WN / 16;                      // blocks that go to y
   constexpr int CLD = BN + 8;                            // epilogue LDS row (bf16)
-  static_assert(WM * WN == 4, "4 waves");
   static_assert(FM * WM * 16 == BM && FNY * WN * 16 == BN, "tile split");
   static_assert(!TX || (PC && WN == 1 && BROWS - BN == 16), "t rows fill the W stage's padding");
   constexpr int ECH = (STAGES * STAGE_BYTES >= BM * CLD * 2) ? BM : BM / 2;  // epilogue rows per pass
@@ -225,19 +235,30 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
   // rank) or -1 at [16 p + c]; [32]: the clamped rank sum
   __shared__ int32_t tmap[TX ? 33 : 1];
 
+  // XCD-aware order: workgroup b runs on XCD b % 8; each XCD gets whole
+  // column strips (every row tile and k half of them), so the workgroups
+  // that read one W strip share that XCD's L2
   const int b = blockIdx.x;
-  const int nblk = p.tiles_m * p.tiles_n;
-  const int t = ((nblk & 7) == 0) ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int ngrid = p.tiles_m * p.tiles_n * SK;
+  const int t = ((ngrid & 7) == 0) ? (b & 7) * (ngrid >> 3) + (b >> 3) : b;
   const int tm = t % p.tiles_m;
-  const int tn = t / p.tiles_m;
+  const int ksp = (t / p.tiles_m) % SK;  // k half of a split-K pair
+  const int tn = t / p.tiles_m / SK;
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const bool producer = PC && wave >= 4;
-  const int pw = wave & 3;  // index among the producers / among the consumers
+  const bool producer = PC && wave >= NC;
+  const int pw = producer ? wave - NC : wave;  // index among the producers / among the consumers
+  // Split-K pairs take the two halves of k (an uneven split, meant to let
+  // one half's partial be written while the other still multiplies,
+  // measured 4 us slower: the longer half sets the end)
+  const int nk_all = p.K / 64;
+  const int nk0 = SK == 2 ? nk_all / 2 : nk_all;
+  const int kt0 = ksp == 0 ? 0 : nk0;                     // first k-tile of this half
+  const uint32_t kbase = (uint32_t)kt0 * 128u;             // its byte offset in a row
 
   const uint32_t a_bytes = (uint32_t)(min(BM, p.M - m0) * p.ldx * 2);
   const uint32_t b_bytes = (uint32_t)(min(BN, p.N - n0) * p.ldw * 2);
@@ -252,7 +273,7 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
     const int P = (pw * A_INSTR + i) * 64 + lane;
     const int row = P >> 3;
     const int c = (P & 7) ^ (row & 7);
-    va[i] = (uint32_t)(row * p.ldx * 2 + c * 16);
+    va[i] = (uint32_t)(row * p.ldx * 2 + c * 16) + kbase;
   }
 #pragma unroll
   for (int i = 0; i < B_INSTR; ++i) {
@@ -260,7 +281,7 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
     const int row = P >> 3;
     const int c = (P & 7) ^ (row & 7);
     // rows past BN (padding of the load pattern) read past the buffer: zeros
-    vb[i] = row < BN ? (uint32_t)(row * p.ldw * 2 + c * 16) : 0xFFFFFFF0u;
+    vb[i] = row < BN ? (uint32_t)(row * p.ldw * 2 + c * 16) + kbase : 0xFFFFFFF0u;
   }
 
   // TX: the producer whose load pattern covers the padding rows builds the
@@ -320,15 +341,15 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
         const int v = row >= BN ? tmap[row - BN] : -1;
         if (v >= 0) {
           const int q = v >> 16, a = (v >> 8) & 255, j = v & 255;
-          tsrc[i] = ft.A[q] + (((int64_t)a * ft.R[q] + j) * p.K) * 2 + c * 16;
+          tsrc[i] = ft.A[q] + (((int64_t)a * ft.R[q] + j) * p.K) * 2 + c * 16 + kbase;
         } else {
-          tsrc[i] = reinterpret_cast<const uint8_t *>(xa) + c * 16;
+          tsrc[i] = reinterpret_cast<const uint8_t *>(xa) + c * 16 + kbase;
         }
       }
     }
   };
 
-  const int nk = p.K / 64;
+  const int nk = ksp == 0 ? nk0 : nk_all - nk0;
   // part: 0 every load of the tile, 1 all but the padding rows, 2 those only
   auto issue = [&](int kt, int stage, int part = 0) {
     uint8_t *sa = smem + stage * STAGE_BYTES;
@@ -359,25 +380,36 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
   const int wm0 = (pw / WN) * (FM * 16);
   const int wn0 = (pw % WN) * (FNY * 16);
 
-  auto compute = [&](int kt) {
-    const uint8_t *sa = smem + (kt % STAGES) * STAGE_BYTES;
-    const uint8_t *sb = sa + A_BYTES;
+  // one k32 step: fragments of this wave's rows and of every column block
+  // (one base offset per operand, the blocks at immediate offsets), then
+  // the FM x FN MFMAs
+  auto kstep = [&](int soff, int ks) {
+    const int pc = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+    int ao = soff + (wm0 + (lane & 15)) * BKB + pc;
+    int bo = soff + A_BYTES + (wn0 + (lane & 15)) * BKB + pc;
+    // opaque to the compiler, which would otherwise hoist one address
+    // register per fragment out of the k loop instead of using the
+    // instructions' immediate offsets
+    asm volatile("" : "+v"(ao), "+v"(bo));
+    bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int pc = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
-      bf16x8_t af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(smem + ao + i * 16 * BKB);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t *>(sa + (wm0 + i * 16 + (lane & 15)) * BKB + pc);
+    for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t *>(smem + bo + j * 16 * BKB);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + (wn0 + j * 16 + (lane & 15)) * BKB + pc);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  auto compute = [&](int kt) {
+    const int soff = (kt % STAGES) * STAGE_BYTES;
+    kstep(soff, 0);
+    // with two MFMA waves per SIMD the other wave covers the fragment
+    // latency; keeping this wave's k32 steps apart holds its registers to
+    // one fragment set
+    if constexpr (NC == 8) __builtin_amdgcn_sched_barrier(0);
+    kstep(soff, 1);
   };
   auto wait_tile = [&](int kt) {
     if (t_loader && kt < STAGES - 2) {
@@ -445,10 +477,68 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
     }
   }
 
+  // The finished tile: the accumulators plus, for a split-K pair, the other
+  // half's partial (added where each block is consumed, so no second
+  // accumulator set is held in registers)
+  const f32x4_t *part_in = nullptr;
+  if constexpr (SK == 2) {
+    // The two k halves of a tile meet here.  The workgroup that arrives
+    // second adds the first one's fp32 partial and runs the epilogue; the
+    // first writes its partial, raises the pair's ready flag and leaves.
+    // Arrival order comes from swapping this launch's epoch into the pair's
+    // arrival word (any other value there means "first"), so no word needs
+    // clearing between calls; only the second waits, and only for a
+    // workgroup that has already arrived.  a + b == b + a in fp32, so the
+    // result does not depend on which half arrives first.
+    const int pair = tm + p.tiles_m * tn;
+    uint64_t *arrive = p.sync + 2 * pair;
+    uint64_t *ready = arrive + 1;
+    f32x4_t *part = reinterpret_cast<f32x4_t *>(p.part) + (size_t)pair * (NC * FM * FN * 64);
+    static_assert(SK == 1 || NC * FM * FN * 64 * 16 <= 8 * 2 * 10 * 64 * 16, "partial fits its slot");
+    __shared__ int s_second;
+    __syncthreads();  // every wave is past its k loop
+    if (tid == 0)  // relaxed: the partial is published through the ready flag
+      s_second = __hip_atomic_exchange(arrive, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 p.epoch;
+    __syncthreads();
+    if (!s_second) {
+      if (!producer) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) part[((pw * FM + i) * FN + j) * 64 + lane] = acc[i][j];
+      }
+      __syncthreads();  // every wave's stores have completed
+      if (tid == 0) {
+        // one release for the workgroup, then the flag
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_store(ready, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    }
+    if (tid == 0) {
+      // relaxed polling (an acquire per poll would invalidate caches each
+      // time), bounded: the first half has arrived, so its flag follows its
+      // partial within microseconds; then one acquire for the workgroup
+      for (int n = 0; n < (1 << 22); ++n) {
+        if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.epoch) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    part_in = part;
+  }
+  const bool owner = !producer;  // the MFMA waves hold the finished tile
+  auto tile_val = [&](int i, int j) -> f32x4_t {
+    if constexpr (SK == 2) return acc[i][j] + part_in[((pw * FM + i) * FN + j) * 64 + lane];
+    return acc[i][j];
+  };
+
   if constexpr (TX) {
     // t: this tile's rows x its 16 t columns, kept where the row's adapter
     // owns the column (tmap was written before the k loop's barriers)
-    if (!producer) {
+    if (owner) {
       const FusedT &ft = p.ft;
       // the rows' ids first (one batch of loads at clamped rows)
       int id[FM][4];
@@ -471,7 +561,7 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
       };
       f32x4_t t0[FM];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) t0[i] = acc[i][FN - 1];
+      for (int i = 0; i < FM; ++i) t0[i] = tile_val(i, FN - 1);
       scatter(tmap[lane & 15], t0);
       if (tmap[32] > ft.cap) {  // uniform
         // second pass: MFMA operands straight from global memory (x rows in
@@ -522,16 +612,18 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int rb = wm0 + i * 16;
-      if (producer || rb < r0 || rb >= r0 + ECH) continue;
+      if (!owner || rb < r0 || rb >= r0 + ECH) continue;
 #pragma unroll
-      for (int j = 0; j < FNY; ++j)
+      for (int j = 0; j < FNY; ++j) {
+        const f32x4_t v = tile_val(i, j);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           ct[(rb - r0 + ((lane >> 4) << 2) + e) * CLD + wn0 + j * 16 + (lane & 15)] =
-              f32_to_bf16_bits(acc[i][j][e]);
+              f32_to_bf16_bits(v[e]);
+      }
     }
     __syncthreads();
-    for (int ch = tid; ch < ECH * CPR; ch += (PC ? 512 : 256)) {
+    for (int ch = tid; ch < ECH * CPR; ch += NT) {
       const int row = ch / CPR;
       const int c = ch - row * CPR;
       const int gm = m0 + r0 + row;
@@ -546,6 +638,18 @@ __global__ __launch_bounds__(PC ? 512 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
       }
     }
   }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool PC, bool TX>
+__global__ __launch_bounds__(PC ? 64 * WM * WN + 256 : 256) void k_gemm_bf16_pipe(PipeArgs p) {
+  pipe_body<BM, BN, WM, WN, STAGES, PC, TX, 1>(p);
+}
+
+// Split-K pairs: at most 160 VGPRs, so three waves per SIMD leave room for
+// the plan kernel (32 VGPRs) that the layer runs beside the GEMM.
+template <bool TX>
+__global__ __launch_bounds__(768) void k_gemm_bf16_split(PipeArgs p) {
+  pipe_body<256, 144, 8, 1, 3, true, TX, 2>(p);
 }
 
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -609,7 +713,7 @@ void launch_pipe(const PipeArgs &pa0, hipStream_t st) {
   // for a second wave per SIMD (at most 128 fp32 per lane)
   constexpr bool PC = (BM / WM) * (BN / WN) / 64 <= 128;
   hipLaunchKernelGGL((k_gemm_bf16_pipe<BM, BN, WM, WN, STAGES, PC, TX>),
-                     dim3(pa.tiles_m * pa.tiles_n), dim3(PC ? 512 : 256), 0, st, pa);
+                     dim3(pa.tiles_m * pa.tiles_n), dim3(PC ? 64 * WM * WN + 256 : 256), 0, st, pa);
 }
 
 bool pipe_ok(int64_t k, int64_t ldx, int64_t ldw) {
@@ -657,18 +761,67 @@ PipeArgs pipe_args(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx, 
   return pa;
 }
 
+// Split-K pairs for the 128 x 144 shapes with more than one 128-row tile
+// (e.g. the 70B q+v decode pair): 256 x 144 tiles, each computed by two
+// workgroups over the two halves of k -- eight MFMA waves plus the four
+// producers per workgroup, the same 256 workgroups as 128 x 144 tiles at
+// 512 rows, but every workgroup streams (256 + 144) x k/2 operand bytes
+// instead of (128 + 144) x k and each W line is shared by two workgroups
+// instead of four (measured at the 70B q+v shape: main loop 81 -> 62 us;
+// the load path, not the MFMAs, bounds it).
+constexpr int kSplitBM = 256, kSplitBN = 144;
+constexpr size_t kSplitPartBytes = (size_t)8 * 2 * 10 * 64 * 16;  // per pair (t block included)
+
+int64_t split_pairs(int64_t M, int64_t d) {
+  return ((M + kSplitBM - 1) / kSplitBM) * ((d + kSplitBN - 1) / kSplitBN);
+}
+size_t split_bytes(int64_t M, int64_t d) {
+  const int64_t P = split_pairs(M, d);
+  return ((size_t)P * kSplitPartBytes + 255) / 256 * 256 + ((size_t)P * 16 + 255) / 256 * 256;
+}
+bool split_ok(int64_t M, int64_t k, int64_t d, void *gws, size_t gws_bytes) {
+  // k >= 256: each half holds at least two k-tiles
+  return gws != nullptr && ((uintptr_t)gws & 255u) == 0 && M > 128 && (k % 128) == 0 && k >= 256 &&
+         gws_bytes >= split_bytes(M, d);
+}
+std::atomic<uint64_t> g_epoch{0x9E3779B97F4A7C15ull};
+template <bool TX>
+void launch_split(PipeArgs pa, int64_t M, int64_t d, void *gws, hipStream_t st) {
+  const int64_t P = split_pairs(M, d);
+  pa.tiles_m = (int)((M + kSplitBM - 1) / kSplitBM);
+  pa.tiles_n = (int)((d + kSplitBN - 1) / kSplitBN);
+  pa.part = reinterpret_cast<float *>(gws);
+  pa.sync = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(gws) +
+                                         ((size_t)P * kSplitPartBytes + 255) / 256 * 256);
+  pa.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
+  hipLaunchKernelGGL(k_gemm_bf16_split<TX>, dim3(pa.tiles_m * pa.tiles_n * 2), dim3(768), 0, st,
+                     pa);
+}
+
 }  // namespace
 
+size_t gemm_ws_bytes(int64_t M, int64_t k, int64_t d) {
+  if (M <= 128 || d <= 0 || (k % 128) != 0 || k < 256 || choose_tile(M, d) != 2) return 0;
+  return split_bytes(M, d);
+}
+
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
-                       const void *W, int64_t ldw, void *y, int64_t ldy, hipStream_t st) {
+                       const void *W, int64_t ldw, void *y, int64_t ldy, void *gws,
+                       size_t gws_bytes, hipStream_t st) {
   if (M <= 0 || d <= 0) return hipSuccess;
   if (dtype == 1) {
     if (pipe_ok(k, ldx, ldw)) {
-      const PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
+      PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
       switch (choose_tile(M, d)) {
         case 0: launch_pipe<256, 256, 2, 2, 2>(pa, st); break;
         case 1: launch_pipe<256, 128, 4, 1, 3>(pa, st); break;
-        case 2: launch_pipe<128, 144, 4, 1, 3>(pa, st); break;
+        case 2:
+          if (split_ok(M, k, d, gws, gws_bytes)) {
+            launch_split<false>(pa, M, d, gws, st);
+          } else {
+            launch_pipe<128, 144, 4, 1, 3>(pa, st);
+          }
+          break;
         case 3: launch_pipe<128, 128, 2, 2, 4>(pa, st); break;
         default: launch_pipe<64, 64, 2, 2, 4>(pa, st); break;
       }
@@ -695,13 +848,17 @@ int32_t gemm_fused_cap(int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw
 
 hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                              const void *W, int64_t ldw, void *y, int64_t ldy, const FusedT &ft,
-                             hipStream_t st) {
+                             void *gws, size_t gws_bytes, hipStream_t st) {
   if (ft.cap <= 0 || ft.cap != gemm_fused_cap(M, k, d, ldx, ldw) ||
       ft.n_slices * ft.S > kFusedMaxEntries || ft.S > 256 || ft.n_slices > kMaxSlices)
     return hipErrorInvalidValue;
   PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
   pa.ft = ft;
-  launch_pipe<128, 144, 4, 1, 3, true>(pa, st);
+  if (split_ok(M, k, d, gws, gws_bytes)) {
+    launch_split<true>(pa, M, d, gws, st);
+  } else {
+    launch_pipe<128, 144, 4, 1, 3, true>(pa, st);
+  }
   return hipGetLastError();
 }
 

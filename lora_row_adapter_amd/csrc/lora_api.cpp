@@ -309,6 +309,11 @@ static lora_status_t check_slices(int32_t n_slices, const lora_slice_t *slices, 
   return LORA_OK;
 }
 
+// The base GEMM's region follows the plan's regions of a chunk of Mc rows.
+static size_t gemm_region_bytes(int64_t Mc, int64_t k, lora_dtype_t dtype, int64_t d_total) {
+  return dtype == LORA_DTYPE_BF16 ? gemm_ws_bytes(Mc, k, d_total) : 0;
+}
+
 size_t lora_workspace_bytes_sliced(int64_t max_rows, int64_t k, lora_dtype_t dtype,
                                    int32_t n_slices, const lora_slice_t *slices) {
   if (max_rows < 0 || k < 1) return 0;
@@ -317,7 +322,12 @@ size_t lora_workspace_bytes_sliced(int64_t max_rows, int64_t k, lora_dtype_t dty
   int64_t dt = 0;
   if (check_slices(n_slices, slices, max_rows, &S, &R, &dt) != LORA_OK) return 0;
   const int64_t rows = std::min<int64_t>(std::max<int64_t>(max_rows, 1), kPlanMaxRows);
-  return ws_layout(rows, S, R, n_slices).total;
+  // any batch of at most max_rows rows: chunks of up to `rows` rows, each
+  // with its plan regions and the GEMM region of its row count
+  size_t need = ws_layout(rows, S, R, n_slices).total + gemm_region_bytes(rows, k, dtype, dt);
+  for (int64_t mc = 256; mc < rows; mc += 256)
+    need = std::max(need, ws_layout(rows, S, R, n_slices).total + gemm_region_bytes(mc, k, dtype, dt));
+  return need;
 }
 
 size_t lora_workspace_bytes(int64_t max_rows, int64_t d, int64_t k, lora_dtype_t dtype,
@@ -330,14 +340,21 @@ size_t lora_workspace_bytes(int64_t max_rows, int64_t d, int64_t k, lora_dtype_t
   return lora_workspace_bytes_sliced(max_rows, k, dtype, 1, &s);
 }
 
+size_t lora_gemm_workspace_bytes(int64_t M, int64_t k, int64_t d, lora_dtype_t dtype) {
+  if (M < 0 || k < 1 || d < 1) return 0;
+  return gemm_region_bytes(M, k, dtype, d);
+}
+
 lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
                         int64_t ldx, const void *W, int64_t ldw, void *y, int64_t ldy,
-                        void *stream) {
+                        void *workspace, size_t workspace_bytes, void *stream) {
   lora_status_t s = check_gemm_args(dtype, M, k, d, x, ldx, W, ldw, y, ldy);
   if (s != LORA_OK || M == 0) return s;
+  if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0) return LORA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(LORA_K_GEMM, st, [&] {
-    return launch_gemm(dtype, M, k, d, x, ldx, W, ldw, y, ldy, st);
+    return launch_gemm(dtype, M, k, d, x, ldx, W, ldw, y, ldy,
+                       workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, st);
   });
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -502,6 +519,11 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
   for (int64_t c0 = 0; c0 < M; c0 += kPlanMaxRows) {
     const int64_t Mc = std::min<int64_t>(kPlanMaxRows, M - c0);
     const WsLayout L = ws_layout(Mc, S, R, n_slices);
+    // the GEMM's region: what the workspace holds past this chunk's plan
+    // regions (a workspace sized by lora_workspace_bytes(_sliced) holds
+    // what every chunk's GEMM uses)
+    void *gws = workspace_bytes > L.total ? (void *)(ws + L.total) : nullptr;
+    const size_t gws_bytes = workspace_bytes > L.total ? workspace_bytes - L.total : 0;
     const uint8_t *xc = (const uint8_t *)x + c0 * ldx * eb;
     uint8_t *yc = (uint8_t *)y + c0 * ldy * eb;
 
@@ -588,8 +610,9 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
     }
     hipError_t e = timed(LORA_K_GEMM, st, [&] {
       if (qw) return launch_gemm_q(make_q_args(qw, Mc, k, d_total, xc, ldx, yc, ldy), st);
-      if (fcap > 0) return launch_gemm_fused(Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, ft, st);
-      return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, st);
+      if (fcap > 0)
+        return launch_gemm_fused(Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, ft, gws, gws_bytes, st);
+      return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, gws, gws_bytes, st);
     });
     if (e != hipSuccess) return LORA_ERR_HIP;
     if (fork && hipStreamWaitEvent(st, ev_join, 0) != hipSuccess) return LORA_ERR_HIP;

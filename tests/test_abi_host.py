@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import lora_row_adapter_amd as lr
 from lora_row_adapter_amd import _binding as B
@@ -24,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("lora_linear", "lora_gemm", "lora_plan", "lora_plan_view", "lora_translate",
+    for required in ("lora_linear", "lora_gemm", "lora_gemm_workspace_bytes", "lora_plan", "lora_plan_view", "lora_translate",
                      "lora_check", "lora_workspace_bytes", "lora_abi_version", "lora_status_str",
                      "lora_profile_enable", "lora_profile_read", "lora_pool_create",
                      "lora_pool_load", "lora_pool_evict", "lora_pool_pin", "lora_pool_unpin",
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lr.abi_version() == 1
+    assert lr.abi_version() == 2
     assert lr.status_str(0) == "ok"
     assert "workspace" in lr.status_str(5)
 
@@ -106,9 +107,11 @@ def test_linear_rejects_bad_arguments_on_host():
 
 def test_gemm_and_misc_reject_bad_arguments_on_host():
     lib = lr.load_library()
-    assert lib.lora_gemm(1, 4, 64, 64, 0, 64, 512, 64, 1024, 64, None) == 1
-    assert lib.lora_gemm(1, 4, 64, 64, 256, 64, 512, 64, 1024, 32, None) == 2
-    assert lib.lora_gemm(1, 0, 64, 64, 0, 64, 0, 64, 0, 64, None) == 0
+    assert lib.lora_gemm(1, 4, 64, 64, 0, 64, 512, 64, 1024, 64, None, 0, None) == 1
+    assert lib.lora_gemm(1, 4, 64, 64, 256, 64, 512, 64, 1024, 32, None, 0, None) == 2
+    assert lib.lora_gemm(1, 0, 64, 64, 0, 64, 0, 64, 0, 64, None, 0, None) == 0
+    # a misaligned workspace is refused before any launch
+    assert lib.lora_gemm(1, 4, 64, 64, 256, 64, 512, 64, 1024, 64, 4096 + 16, 1 << 20, None) == 5
     assert lib.lora_check(None, None, None, None, None) == 1
     c = _slots_struct()
     assert lib.lora_translate(ctypes.byref(c), 16, 16, 4, 16, None) == 1   # slots have no pages
@@ -126,3 +129,28 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_HERE", str(tmp_path))
     with pytest.raises(RuntimeError, match="not built"):
         B.load_library()
+
+
+def test_gemm_workspace_sizes():
+    """Split-K pairs (256 x 144 tiles, two k halves) at shapes that would run
+    128 x 144 tiles with more than 128 rows: per pair 8 waves x 2 x 10 MFMA
+    blocks of 64 lanes x 16 bytes, plus 16 bytes of arrival/ready words, each
+    region 256-byte aligned."""
+    bf16 = 1
+    pairs = 2 * 64  # 512 rows, d = 9216
+    part = pairs * 8 * 2 * 10 * 64 * 16
+    assert lr.gemm_workspace_bytes(512, 8192, 9216, torch.bfloat16) == part + 2048
+    assert lr.gemm_workspace_bytes(128, 8192, 9216, torch.bfloat16) == 0   # one row tile
+    assert lr.gemm_workspace_bytes(512, 8192, 4096, torch.bfloat16) == 0   # not a 144-column shape
+    assert lr.gemm_workspace_bytes(512, 8192, 9216, torch.float32) == 0
+    assert lr.gemm_workspace_bytes(400, 8192, 9216, torch.bfloat16) == part + 2048  # ragged rows
+    assert lr.gemm_workspace_bytes(384, 8192, 9216, torch.bfloat16) == 0  # 128 x 128 tiles fit one round
+    lib = lr.load_library()
+    assert lib.lora_gemm_workspace_bytes(512, 8192 + 64, 9216, bf16) == 0  # k halves not 64-aligned
+    # the layer's workspace holds the GEMM region of every chunk it may run
+    c = _slots_struct(S=12, R=64)
+    small = lib.lora_workspace_bytes(128, 9216, 8192, bf16, ctypes.byref(c))
+    full = lib.lora_workspace_bytes(512, 9216, 8192, bf16, ctypes.byref(c))
+    assert full >= small + part
+    # fp32 layers run no split GEMM
+    assert lib.lora_workspace_bytes(512, 9216, 8192, 0, ctypes.byref(c)) < small + part
