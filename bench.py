@@ -6,8 +6,9 @@ of one attention layer, for 512 rows with 12 adapters of rank {4 x3, 16 x6,
 64 x3} (alpha = 2r, Zipf 1.1 popularity, 10% rows without adapter), bf16
 with fp32 accumulation.  Both projections share x and the per-row adapter
 ids, so they run as one multi-slice call: plan, one base GEMM over the
-stacked [9216, 8192] weight that also computes the shrink (t = x A^T for
-every adapter rank, folded into its tiles), one expand.  The shrink as its
+stacked [9216, 8192] weight (256 x 144 tiles, each computed by two
+workgroups over the two halves of k) that also computes the shrink
+(t = x A^T for every adapter rank, folded into its tiles), one expand.  The shrink as its
 own kernel (x read once for both slices) is timed in a second pass with the
 folding turned off (kernels.separate_shrink_step, kernels.shrink_gbs).
 
@@ -256,9 +257,11 @@ def main():
             "buffer_set_mb": round(set_bytes / 1e6, 1),
         },
         "roofline": {
-            "kernel": ("k_gemm_bf16_pipe (base GEMM over the stacked q+v weight, shrink folded in; "
-                       "achieved counts the base GEMM's and the shrink's algorithmic flops)"
-                       if folded else "k_gemm_bf16_pipe (base GEMM over the stacked q+v weight)"),
+            "kernel": ("k_gemm_bf16_split<true> (base GEMM over the stacked q+v weight as split-K "
+                       "workgroup pairs, shrink folded in; achieved counts the base GEMM's and the "
+                       "shrink's algorithmic flops)"
+                       if folded else "k_gemm_bf16_split<false> (base GEMM over the stacked q+v "
+                       "weight as split-K workgroup pairs)"),
             "bound": "mfma",
             "achieved": gemm_tflops,
             "peak": BF16_PEAK_TFLOPS,

@@ -320,16 +320,20 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   __shared__ __attribute__((aligned(16))) float ys[16 * YLD];
 
   // Workgroup b runs on XCD b % 8.  A column block stays on one XCD for
-  // every item (cb = b % 8 + 8 * j), so the items of one adapter -- which
-  // read the same B rows -- share that XCD's L2 instead of each fetching
-  // B (whole 128-byte lines even for a small rank) from memory.
+  // every item, so the items of one adapter -- which read the same B rows
+  // -- share that XCD's L2 instead of each fetching B (whole 128-byte lines
+  // even for a small rank) from memory.  XCD x takes the blocks of columns
+  // [x d / 8, (x + 1) d / 8): the base GEMM's tile order gives each XCD the
+  // same eighth of y's columns, so the y rows this kernel updates are still
+  // in that XCD's L2.
   const int ncb = a.col_blk[a.n_slices];
   const int per_xcd = (ncb + 7) >> 3;
   const int b = blockIdx.x;
   const int q = b >> 3;
   const int item = q / per_xcd;
-  const int cbk = (b & 7) + 8 * (q - item * per_xcd);
-  if (cbk >= ncb) return;
+  const int xcd = b & 7;
+  const int cbk = ((xcd * ncb) >> 3) + (q - item * per_xcd);
+  if (cbk >= (((xcd + 1) * ncb) >> 3)) return;
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
   // the item slot exists up to the list's capacity, so it is read beside
   // the count instead of after it
