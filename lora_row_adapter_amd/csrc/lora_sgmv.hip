@@ -307,7 +307,7 @@ __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int keep) {
 // bound by the address path of the vector memory unit, where clamped lanes
 // cost as much as real ones (measured slower with clamping).
 template <int RB, int ECB, bool FAST>
-__global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
+__device__ __forceinline__ void expand_body(const LoraArgs &a) {
   constexpr int RBK = RB / 16;
   constexpr int KP = RMAX_MFMA + 8;  // padded LDS row (bf16)
   constexpr int CB = ECB / 64;       // 16-column blocks per wave
@@ -554,6 +554,18 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LoraArgs a) {
   }
 }
 
+// 16-row items (decode batches).  (Capping its registers so that 4-6
+// workgroups fit per CU instead of 3 measured no faster at 4 and twice as
+// slow at 5-6, where it spills.)
+template <int ECB, bool FAST>
+__global__ __launch_bounds__(256) void k_expand_mfma16(LoraArgs a) {
+  expand_body<16, ECB, FAST>(a);
+}
+template <bool FAST>
+__global__ __launch_bounds__(256) void k_expand_mfma64(LoraArgs a) {
+  expand_body<64, 256, FAST>(a);
+}
+
 }  // namespace
 
 hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_slice,
@@ -583,12 +595,12 @@ hipError_t launch_expand_sgmv(const LoraArgs &a0, int rows_per_item, hipStream_t
            a.sl[q].col0 % 8 == 0;
   if (rows_per_item == 16) {
     const dim3 grid((unsigned)(a.L.items_g_cap * cb8));
-    if (fast) hipLaunchKernelGGL((k_expand_mfma<16, kExpandCols16, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_expand_mfma<16, kExpandCols16, false>), grid, dim3(256), 0, st, a);
+    if (fast) hipLaunchKernelGGL((k_expand_mfma16<kExpandCols16, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_expand_mfma16<kExpandCols16, false>), grid, dim3(256), 0, st, a);
   } else {
     const dim3 grid((unsigned)(a.L.items_s_cap * cb8));
-    if (fast) hipLaunchKernelGGL((k_expand_mfma<64, 256, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_expand_mfma<64, 256, false>), grid, dim3(256), 0, st, a);
+    if (fast) hipLaunchKernelGGL((k_expand_mfma64<true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_expand_mfma64<false>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
