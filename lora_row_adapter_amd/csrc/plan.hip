@@ -6,6 +6,10 @@ namespace lora {
 
 namespace {
 
+// The layer runs this kernel on a side stream beside its base GEMM, whose
+// split-K workgroups hold three waves of 160 VGPRs per SIMD: it keeps
+// running there only while it needs at most 32 VGPRs (at 40 it waited for
+// the GEMM to finish and the 70B q+v step lost ~10%).
 template <int NT>
 __global__ __launch_bounds__(NT) void k_plan(PlanArgs a, uint32_t lds_bytes) {
   extern __shared__ __attribute__((aligned(16))) uint8_t plan_lds[];
