@@ -70,6 +70,8 @@ def parse():
                     help="skip the merged-weight (lora_merge) measurement")
     ap.add_argument("--no-quant", action="store_true",
                     help="skip the INT8 / INT4 base-weight measurement")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the decode-4096, prefill and paged-pool workloads")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/ summaries from a rocprofv3 run whose trace/, fetch/, "
                          "write/, cfetch/, cwrite/ output directories are under DIR, and exit")
@@ -293,9 +295,83 @@ def main():
         result["merge"] = merge_rate(lr, w, pq, pv, sets, stream)
     if not args.no_quant:
         result["quantized_base"] = quantized_rate(lr, wl, w, sets, ids, ws, stream, args)
+    if not args.no_others:
+        result["other_configs"] = other_configs(lr, wl, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, pq, pv, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def other_configs(lr, wl, stream, n_sets=4, steps=200, warmup=100):
+    """The other seeded workloads, one lora_linear call per step, rotating x,
+    W and y over n_sets buffer sets (adapters: one copy -- the c4 pool holds
+    1024 adapters in 2 MiB pages):
+      c1_decode_bf16   256 rows, d = k = 4096, 4 slots of rank 16
+      c2_prefill_bf16  8 x 1024 rows, d = k = 4096, ranks 8..64 padded to 64,
+                       one adapter per sequence (contiguous runs: 64-row SGMV items)
+      c4_paged_bf16    2048 rows from 256 sequences, d = k = 5120, 1024 adapters
+                       of rank 16 in a paged pool, ~131 present
+    Per workload: tokens/s, event-timed launches, the base GEMM's TFLOP/s and
+    the shrink / expand GB/s against the algorithmic bytes of the instance."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for name, make, storage in (("c1_decode_bf16", wl.c1_decode_bf16, "slots"),
+                                ("c2_prefill_bf16", wl.c2_prefill_bf16, "slots"),
+                                ("c4_paged_bf16", wl.c4_paged_bf16, "pool")):
+        w = make()
+        p = w.projections[0]
+        M = w.M
+        ids = torch.from_numpy(w.ids).to(dev)
+        scales = torch.from_numpy(w.scales).to(dev)
+        ranks = torch.from_numpy(w.ranks).to(dev)
+        if storage == "slots":
+            A, B = wl.slots(w, p)
+            ad = lr.Adapters.slots(A.to(dev), B.to(dev), ranks)
+        else:
+            pool, table, _ = wl.pool(w, p)
+            ad = lr.Adapters.paged(pool.to(dev), table.to(dev), ranks, w.page_bytes, w.max_rank)
+        x0, W0 = w.x.to(dev), p.W.to(dev)
+        xs = [x0] + [x0.clone() for _ in range(n_sets - 1)]
+        Ws = [W0] + [W0.clone() for _ in range(n_sets - 1)]
+        ys = [torch.empty(M, p.d, dtype=w.dtype, device=dev) for _ in range(n_sets)]
+        ws = lr.new_workspace(M, p.d, w.k, w.dtype, ad, device=dev)
+
+        def step(i):
+            lr.lora_linear(xs[i % n_sets], Ws[i % n_sets], ad, ids, scales, y=ys[i % n_sets],
+                           workspace=ws, stream=stream)
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        with lr.Profiler():
+            for i in range(steps):
+                step(i)
+            prof = lr.Profiler.read(reset=True)
+            torch.cuda.synchronize()
+        per = {kn: prof[kn]["ms"] * 1e3 / prof[kn]["launches"] for kn in lr.KERNEL_CLASSES
+               if prof[kn]["launches"]}
+        alg = wl.algorithmic_bytes(w, p)
+        shr = per.get("sgmv_shrink", per.get("shrink"))
+        exp = per.get("sgmv_expand", per.get("expand"))
+        gemm = per.get("gemm")
+        out[name] = {
+            "rows": M, "d": p.d, "k": w.k, "adapter_storage": storage, "n_present": alg["n_present"],
+            "adapted_rows": alg["M_a"],
+            "tokens_per_s": round(M * steps / el, 1), "ms_per_step": round(el * 1e3 / steps, 4),
+            "per_launch_us": {kn: round(v, 2) for kn, v in per.items()},
+            "gemm_tflops": round(alg["gemm_flops"] / gemm / 1e6, 1) if gemm else None,
+            "gemm_frac_bf16_peak": round(alg["gemm_flops"] / gemm / 1e6 / BF16_PEAK_TFLOPS, 4) if gemm else None,
+            "shrink_gbs": round(alg["shrink_bytes"] / shr / 1e3, 1) if shr else None,
+            "expand_gbs": round(alg["expand_bytes"] / exp / 1e3, 1) if exp else None,
+        }
+        log("%s: %s" % (name, json.dumps(out[name])))
+        del xs, Ws, ys, ws, ad
+        torch.cuda.empty_cache()
+    return out
 
 
 def quantized_rate(lr, wl, w, sets, ids, ws, stream, args):
