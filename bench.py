@@ -259,10 +259,10 @@ def main():
             "buffer_set_mb": round(set_bytes / 1e6, 1),
         },
         "roofline": {
-            "kernel": ("k_gemm_bf16_split<true> (base GEMM over the stacked q+v weight as split-K "
+            "kernel": ("k_gemm_bf16_split<144, true, 2> (base GEMM over the stacked q+v weight as split-K "
                        "workgroup pairs, shrink folded in; achieved counts the base GEMM's and the "
                        "shrink's algorithmic flops)"
-                       if folded else "k_gemm_bf16_split<false> (base GEMM over the stacked q+v "
+                       if folded else "k_gemm_bf16_split<144, false, 2> (base GEMM over the stacked q+v "
                        "weight as split-K workgroup pairs)"),
             "bound": "mfma",
             "achieved": gemm_tflops,

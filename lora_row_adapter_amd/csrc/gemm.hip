@@ -663,11 +663,13 @@ __global__ __launch_bounds__(PC ? 64 * WM * WN + 256 : 256) void k_gemm_bf16_pip
   pipe_body<BM, BN, WM, WN, STAGES, PC, TX, 1>(p);
 }
 
-// Split-K pairs: at most 160 VGPRs, so three waves per SIMD leave room for
+// 256-row tiles with eight MFMA waves (32 x BN each) beside the four
+// producers: split-K pairs (SK = 2) over 256 x 144 tiles, and unsplit
+// 256 x 160 tiles.  At most 160 VGPRs, so three waves per SIMD leave room for
 // the plan kernel (32 VGPRs) that the layer runs beside the GEMM.
-template <bool TX>
+template <int BN, bool TX, int SK>
 __global__ __launch_bounds__(768) void k_gemm_bf16_split(PipeArgs p) {
-  pipe_body<256, 144, 8, 1, 3, true, TX, 2>(p);
+  pipe_body<256, BN, 8, 1, 3, true, TX, SK>(p);
 }
 
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -746,12 +748,12 @@ bool pipe_ok(int64_t k, int64_t ldx, int64_t ldw) {
 int choose_tile(int64_t M, int64_t d) {
   struct Cand { int bm, bn; double cost; };
   const Cand cands[] = {{256, 256, 0.87}, {256, 128, 0.90}, {128, 144, 0.97},
-                        {128, 128, 1.00}, {64, 64, 2.2}};
+                        {128, 128, 1.00}, {64, 64, 2.2},   {256, 160, 0.92}};
   int best = 3;
   double best_t = 1e30;
-  for (int c = 0; c < 5; ++c) {
+  for (int c = 0; c < 6; ++c) {
     const Cand &cd = cands[c];
-    if (cd.bn == 144 && d % 144 != 0) continue;
+    if ((cd.bn == 144 && d % 144 != 0) || (cd.bn == 160 && d % 160 != 0)) continue;
     const int64_t tiles = ((M + cd.bm - 1) / cd.bm) * ((d + cd.bn - 1) / cd.bn);
     const int64_t rounds = (tiles + 255) / 256;
     const double t_est = (double)rounds * cd.bm * cd.bn * cd.cost;
@@ -808,12 +810,21 @@ void launch_split(PipeArgs pa, int64_t M, int64_t d, void *gws, hipStream_t st) 
   const int64_t P = split_pairs(M, d);
   pa.tiles_m = (int)((M + kSplitBM - 1) / kSplitBM);
   pa.tiles_n = (int)((d + kSplitBN - 1) / kSplitBN);
+  static_assert(kSplitBN == 144, "split-K pairs use 256 x 144 tiles");
   pa.part = reinterpret_cast<float *>(gws);
   pa.sync = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(gws) +
                                          ((size_t)P * kSplitPartBytes + 255) / 256 * 256);
   pa.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
-  hipLaunchKernelGGL(k_gemm_bf16_split<TX>, dim3(pa.tiles_m * pa.tiles_n * 2), dim3(768), 0, st,
-                     pa);
+  hipLaunchKernelGGL((k_gemm_bf16_split<144, TX, 2>), dim3(pa.tiles_m * pa.tiles_n * 2), dim3(768),
+                     0, st, pa);
+}
+// Unsplit 256 x 160 tiles (e.g. 2048 rows x 5120 columns: 256 tiles, where
+// 256 x 256 tiles leave 96 CUs idle)
+void launch_wide(PipeArgs pa, int64_t M, int64_t d, hipStream_t st) {
+  pa.tiles_m = (int)((M + 255) / 256);
+  pa.tiles_n = (int)((d + 159) / 160);
+  hipLaunchKernelGGL((k_gemm_bf16_split<160, false, 1>), dim3(pa.tiles_m * pa.tiles_n), dim3(768),
+                     0, st, pa);
 }
 
 }  // namespace
@@ -841,6 +852,7 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
           }
           break;
         case 3: launch_pipe<128, 128, 2, 2, 4>(pa, st); break;
+        case 5: launch_wide(pa, M, d, st); break;
         default: launch_pipe<64, 64, 2, 2, 4>(pa, st); break;
       }
       return hipGetLastError();
@@ -862,6 +874,52 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
 int32_t gemm_fused_cap(int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw) {
   if (M <= 0 || d <= 0 || !pipe_ok(k, ldx, ldw) || choose_tile(M, d) != 2) return 0;
   return (int32_t)(16 * ((d + 143) / 144));
+}
+
+// The kernel and block size launch_gemm / launch_gemm_fused would run.
+static void gemm_pick(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
+                      bool split, bool fused, const void **fn, int *threads) {
+  *threads = 256;
+  if (dtype != 1) {
+    *fn = (const void *)k_gemm_f32;
+    return;
+  }
+  if (!pipe_ok(k, ldx, ldw)) {
+    *fn = (const void *)k_gemm_bf16;
+    return;
+  }
+  switch (fused ? 2 : choose_tile(M, d)) {
+    case 0: *fn = (const void *)k_gemm_bf16_pipe<256, 256, 2, 2, 2, false, false>; break;
+    case 1: *fn = (const void *)k_gemm_bf16_pipe<256, 128, 4, 1, 3, true, false>; *threads = 512; break;
+    case 2:
+      if (split) {
+        *fn = fused ? (const void *)k_gemm_bf16_split<144, true, 2>
+                    : (const void *)k_gemm_bf16_split<144, false, 2>;
+        *threads = 768;
+      } else {
+        *fn = fused ? (const void *)k_gemm_bf16_pipe<128, 144, 4, 1, 3, true, true>
+                    : (const void *)k_gemm_bf16_pipe<128, 144, 4, 1, 3, true, false>;
+        *threads = 512;
+      }
+      break;
+    case 3: *fn = (const void *)k_gemm_bf16_pipe<128, 128, 2, 2, 4, true, false>; *threads = 512; break;
+    case 5: *fn = (const void *)k_gemm_bf16_split<160, false, 1>; *threads = 768; break;
+    default: *fn = (const void *)k_gemm_bf16_pipe<64, 64, 2, 2, 4, true, false>; *threads = 512; break;
+  }
+}
+
+bool gemm_footprint(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
+                    void *gws, size_t gws_bytes, bool fused, KernelFootprint *out) {
+  const void *fn = nullptr;
+  int threads = 256;
+  gemm_pick(dtype, M, k, d, ldx, ldw, dtype == 1 && split_ok(M, k, d, gws, gws_bytes), fused, &fn,
+            &threads);
+  hipFuncAttributes at{};
+  if (!kernel_attributes(fn, &at)) return false;
+  out->threads = threads;
+  out->vgprs = at.numRegs;
+  out->lds = at.sharedSizeBytes;
+  return true;
 }
 
 hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,

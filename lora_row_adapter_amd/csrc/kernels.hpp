@@ -66,7 +66,31 @@ struct LoraArgs {
   int32_t fused_cap;
 };
 
-hipError_t launch_plan(const PlanArgs &a, hipStream_t st);
+// max_lds: dynamic LDS the plan may take -- kPlanLdsBeside when it runs
+// beside a GEMM, kPlanLdsAlone when it has the CU to itself (the 1024-thread
+// counting sort then serves more adapters)
+constexpr size_t kPlanLdsBeside = 65536, kPlanLdsAlone = 152 * 1024;
+hipError_t launch_plan(const PlanArgs &a, hipStream_t st, size_t max_lds = kPlanLdsBeside);
+
+// Resources of one workgroup of a kernel: threads, VGPRs per lane (arch +
+// accumulation registers), LDS bytes (static + dynamic).
+struct KernelFootprint {
+  int threads = 0;
+  int vgprs = 0;
+  size_t lds = 0;
+};
+// hipFuncGetAttributes of a kernel, cached (the library is built for one
+// architecture, so the attributes do not depend on the device).
+bool kernel_attributes(const void *fn, hipFuncAttributes *out);
+// What launch_plan would launch for these arguments.
+bool plan_footprint(const PlanArgs &a, KernelFootprint *out);
+// What launch_gemm (fused = false) or launch_gemm_fused (true) would launch.
+bool gemm_footprint(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
+                    void *gws, size_t gws_bytes, bool fused, KernelFootprint *out);
+// Whether a workgroup of `b` fits on a CU beside one workgroup of `a`
+// (gfx950: 4 SIMDs of 512 VGPRs per lane, VGPRs allocated in blocks of 8,
+// 160 KiB of LDS).
+bool fits_beside(const KernelFootprint &a, const KernelFootprint &b);
 hipError_t launch_translate(const AdapterRef &ar, int32_t S, int64_t n_pages,
                             const int32_t *adapter, const int64_t *off, int64_t n,
                             int64_t *phys, hipStream_t st);

@@ -399,9 +399,10 @@ static PlanArgs make_plan_args(int64_t M, int64_t k, lora_dtype_t dtype, int32_t
 
 static lora_status_t run_plan(int64_t M, int64_t k, lora_dtype_t dtype, int32_t n_slices,
                               const lora_slice_t *slices, const int32_t *ids, uint8_t *ws,
-                              const WsLayout &L, hipStream_t st) {
+                              const WsLayout &L, hipStream_t st,
+                              size_t max_lds = kPlanLdsBeside) {
   const PlanArgs p = make_plan_args(M, k, dtype, n_slices, slices, ids, ws, L);
-  hipError_t e = timed(LORA_K_PLAN, st, [&] { return launch_plan(p, st); });
+  hipError_t e = timed(LORA_K_PLAN, st, [&] { return launch_plan(p, st, max_lds); });
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -595,16 +596,29 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
     // only the GEMM's leftover CU resources and finishes later than after
     // it.)  Later calls on the caller's stream are ordered after this call
     // by the fork event, so the workspace is never rewritten while read.
+    // The plan runs beside the GEMM only where one of its workgroups fits on a
+    // CU next to one of the GEMM's (registers and LDS); otherwise it would
+    // wait for GEMM workgroups to finish and then hold up the shrink, so it
+    // runs on the caller's stream ahead of the GEMM.
     hipStream_t ps = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     const bool reuse = (flags & LORA_FLAG_REUSE_PLAN) != 0;
-    const bool fork = !reuse && side::get(&ps, &ev_fork, &ev_join);
+    bool beside = true;
+    if (!reuse && !qw) {
+      KernelFootprint pf, gf;
+      const PlanArgs pa = make_plan_args(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L);
+      beside = plan_footprint(pa, &pf) &&
+               gemm_footprint(dtype, Mc, k, d_total, ldx, ldw, gws, gws_bytes, fcap > 0, &gf) &&
+               fits_beside(gf, pf);
+    }
+    const bool fork = !reuse && beside && side::get(&ps, &ev_fork, &ev_join);
     if (!reuse) {
       if (fork) {
         if (hipEventRecord(ev_fork, st) != hipSuccess || hipStreamWaitEvent(ps, ev_fork, 0) != hipSuccess)
           return LORA_ERR_HIP;
       }
-      s = run_plan(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L, fork ? ps : st);
+      s = run_plan(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L, fork ? ps : st,
+                   fork || beside ? kPlanLdsBeside : kPlanLdsAlone);
       if (s != LORA_OK) return s;
       if (fork && hipEventRecord(ev_join, ps) != hipSuccess) return LORA_ERR_HIP;
     }

@@ -1,5 +1,8 @@
 // plan.hip -- the plan kernel (for lora_plan and for base GEMMs that cannot
 // carry the plan in their own launch) and the page-table translation kernel.
+#include <mutex>
+#include <unordered_map>
+
 #include "plan_body.hpp"
 
 namespace lora {
@@ -36,32 +39,69 @@ __global__ __launch_bounds__(256) void k_translate(AdapterRef ar, int32_t S, int
 
 }  // namespace
 
-hipError_t launch_plan(const PlanArgs &a, hipStream_t st) {
-  // LDS sized to the batch: the counting sort where its per-wave histograms
-  // fit in 64 KiB (with 1024 threads for large batches, else 256), else the
-  // bitonic sort (256 threads up to 1024 sort slots, else 1024)
-  constexpr size_t kMaxLds = 65536;
+// LDS sized to the batch: the counting sort where its per-wave histograms
+// fit in kMaxLds (with 1024 threads for large batches, else 256), else the
+// bitonic sort (256 threads up to 1024 sort slots, else 1024)
+static void plan_shape(const PlanArgs &a, size_t kMaxLds, int *nt, size_t *lds) {
   const bool large = (1 << a.row_bits) > 1024;
   const size_t c1024 = plan_detail::plan_count_lds(a.M, a.S, kPlanThreads);
   const size_t c256 = plan_detail::plan_count_lds(a.M, a.S, 256);
+  if (large && c1024 <= kMaxLds) {
+    *nt = kPlanThreads;
+    *lds = c1024;
+  } else if (c256 <= kMaxLds) {
+    *nt = 256;
+    *lds = c256;
+  } else {
+    *nt = large ? kPlanThreads : 256;
+    *lds = plan_detail::plan_sort_lds(a.row_bits);
+  }
+}
+
+hipError_t launch_plan(const PlanArgs &a, hipStream_t st, size_t max_lds) {
   int nt;
   size_t lds;
-  if (large && c1024 <= kMaxLds) {
-    nt = kPlanThreads;
-    lds = c1024;
-  } else if (c256 <= kMaxLds) {
-    nt = 256;
-    lds = c256;
-  } else {
-    nt = large ? kPlanThreads : 256;
-    lds = plan_detail::plan_sort_lds(a.row_bits);
-  }
+  plan_shape(a, max_lds, &nt, &lds);
   if (nt == 256)
     hipLaunchKernelGGL(k_plan<256>, dim3(1), dim3(256), lds, st, a, (uint32_t)lds);
   else
     hipLaunchKernelGGL(k_plan<kPlanThreads>, dim3(1), dim3(kPlanThreads), lds, st, a,
                        (uint32_t)lds);
   return hipGetLastError();
+}
+
+bool kernel_attributes(const void *fn, hipFuncAttributes *out) {
+  static std::mutex mu;
+  static std::unordered_map<const void *, hipFuncAttributes> cache;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = cache.find(fn);
+  if (it == cache.end()) {
+    hipFuncAttributes at{};
+    if (hipFuncGetAttributes(&at, fn) != hipSuccess) return false;
+    it = cache.emplace(fn, at).first;
+  }
+  *out = it->second;
+  return true;
+}
+
+bool plan_footprint(const PlanArgs &a, KernelFootprint *out) {
+  int nt;
+  size_t lds;
+  plan_shape(a, kPlanLdsBeside, &nt, &lds);
+  hipFuncAttributes at{};
+  if (!kernel_attributes(nt == 256 ? (const void *)k_plan<256> : (const void *)k_plan<kPlanThreads>, &at))
+    return false;
+  out->threads = nt;
+  out->vgprs = at.numRegs;
+  out->lds = at.sharedSizeBytes + lds;
+  return true;
+}
+
+bool fits_beside(const KernelFootprint &a, const KernelFootprint &b) {
+  auto waves_per_simd = [](int threads) { return ((threads + 63) / 64 + 3) / 4; };
+  auto alloc = [](int v) { return (v + 7) / 8 * 8; };
+  const int vg = waves_per_simd(a.threads) * alloc(a.vgprs) + waves_per_simd(b.threads) * alloc(b.vgprs);
+  return vg <= 512 && a.lds + b.lds <= 160 * 1024;
 }
 
 hipError_t launch_translate(const AdapterRef &ar, int32_t S, int64_t n_pages,

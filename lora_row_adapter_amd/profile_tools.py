@@ -111,9 +111,9 @@ def summarize(root: str, out_dir: str, bench_cmd: str, copy_mib: int, gemm_sourc
     open(md, "w").write("\n".join(lines) + "\n")
     # the headline step's GEMM: the split-K pairs with the shrink folded in
     # (template argument true), then the plain split, then unsplit tiles
-    gemm = sorted((k for k in traffic if k.startswith("k_gemm_bf16_split") or
+    gemm = sorted((k for k in traffic if k.startswith("k_gemm_bf16_split<144") or
                    k.startswith("k_gemm_bf16_pipe")),
-                  key=lambda k: (not k.startswith("k_gemm_bf16_split"), not k.endswith("true>"), k))
+                  key=lambda k: (not k.startswith("k_gemm_bf16_split"), "true" not in k, k))
     result = {"workload": workload, "kernel_trace": stats, "traffic": traffic,
               "fetch_factor": f_fac, "write_factor": w_fac}
     if gemm:

@@ -1,6 +1,7 @@
 """Split-K workgroup pairs of the base GEMM (256 x 144 tiles, each computed by
 two workgroups over the two halves of k; the second to arrive adds the
-first one's fp32 partial from the workspace).
+first one's fp32 partial from the workspace), and the unsplit 256 x 160
+tiles of the same eight-wave kernel.
 
 They run where the GEMM would otherwise use 128 x 144 tiles with more than
 one 128-row tile -- e.g. 385..512 rows with d in (8192, 9216] -- and only
@@ -98,6 +99,18 @@ def test_small_workspace_falls_back_to_unsplit_tiles():
     y_plain = lr.lora_gemm(xd, Wd, workspace=_no_workspace())
     torch.cuda.synchronize()
     assert torch.equal(y_short, y_plain)
+
+
+@pytest.mark.parametrize("M,k,d", [(2048, 256, 5120), (1900, 320, 5120)])
+def test_wide_tiles_match_fp64(M, k, d):
+    """Unsplit 256 x 160 tiles (2048 rows x 5120 columns: 256 tiles), with a
+    ragged last row tile; no workspace involved."""
+    say("wide-tile gemm M=%d k=%d d=%d" % (M, k, d))
+    assert lr.gemm_workspace_bytes(M, k, d, torch.bfloat16) == 0
+    x, W = _operands(M, k, d, 17 + M)
+    y = lr.lora_gemm(x.cuda(), W.cuda())
+    torch.cuda.synchronize()
+    assert normwise(y.double().cpu().numpy(), _ref(x, W)) <= TOL
 
 
 def test_layer_none_rows_equal_split_gemm_bitwise():
