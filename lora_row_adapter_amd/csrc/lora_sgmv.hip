@@ -227,8 +227,13 @@ __device__ __forceinline__ void shrink_blocks(const LoraArgs &a, const Item &it,
   }
 }
 
-// grid (item, k split): x rows are loaded once for every slice's A.
-template <int RB>
+// grid (item, slice or all slices, k split).  PER_SLICE: one slice per
+// workgroup, at most 4 rank blocks (ranks <= 64), so only the 4-block path
+// is compiled and it alone sets the register budget (64-row items: 422 ->
+// 212 VGPRs, two waves per SIMD; with one k step per round the 8192-row
+// prefill shrink went 31.4 -> 23.4 us, 2 or 4 steps per round 24.8 / 25.2 us).
+constexpr int kShrinkSteps64 = 1;
+template <int RB, bool PER_SLICE>
 __global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
   constexpr int RBK = RB / 16;
   __shared__ f32x4_t red[4][4][64];
@@ -274,9 +279,9 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
   // block groups sized so that few blocks keep several k steps of loads
   // in flight; up to 8 blocks (two projections of rank 64) share one read
   // of the x rows, more take another pass over them
-  if (vhi - vlo <= 4) {
-    shrink_blocks<RB, 4, 4>(a, it, rk, vlo, vhi, kbeg, kend, xoff, xv, red);
-  } else {
+  if (PER_SLICE || vhi - vlo <= 4) {
+    shrink_blocks<RB, 4, RB == 64 ? kShrinkSteps64 : 4>(a, it, rk, vlo, vhi, kbeg, kend, xoff, xv, red);
+  } else if constexpr (!PER_SLICE) {
     for (int v0 = vlo; v0 < vhi; v0 += 8)
       shrink_blocks<RB, 8, RB == 16 ? 2 : 1>(a, it, rk, v0, vhi, kbeg, kend, xoff, xv, red);
   }
@@ -571,12 +576,15 @@ __global__ __launch_bounds__(256) void k_expand_mfma64(LoraArgs a) {
 hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_slice,
                               hipStream_t st) {
   const unsigned gy = per_slice ? (unsigned)a.n_slices : 1u;
+  // per slice: at most 4 rank blocks per workgroup (ranks <= 64)
   if (rows_per_item == 16) {
     dim3 grid((unsigned)a.L.items_g_cap, gy, (unsigned)a.ksplit);
-    hipLaunchKernelGGL(k_shrink_mfma<16>, grid, dim3(256), 0, st, a);
+    if (per_slice) hipLaunchKernelGGL((k_shrink_mfma<16, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_shrink_mfma<16, false>), grid, dim3(256), 0, st, a);
   } else {
     dim3 grid((unsigned)a.L.items_s_cap, gy, (unsigned)a.ksplit);
-    hipLaunchKernelGGL(k_shrink_mfma<64>, grid, dim3(256), 0, st, a);
+    if (per_slice) hipLaunchKernelGGL((k_shrink_mfma<64, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_shrink_mfma<64, false>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
