@@ -109,8 +109,8 @@ def main():
         print(json.dumps({k: v for k, v in res.items() if k != "kernel_trace"}, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the layer is row-independent and this build runs on a "
-              "single MI355X (--gpus %d requested); see DESIGN.md for how it would shard."
+        print("bench.py measures one GPU (--gpus %d requested): the layer is row-independent, "
+              "and a run over several GPUs is not provided."
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 

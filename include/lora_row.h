@@ -64,7 +64,7 @@ typedef enum lora_status {
   LORA_ERR_WORKSPACE = 5,   /* workspace too small or misaligned */
   LORA_ERR_PAGE = 6,        /* pool geometry invalid (page size, counts) */
   LORA_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
-  LORA_ERR_UNSUPPORTED = 8  /* valid request that this build does not implement */
+  LORA_ERR_UNSUPPORTED = 8  /* valid request that this library does not implement */
 } lora_status_t;
 
 typedef enum lora_dtype {

@@ -283,7 +283,7 @@ const char *lora_status_str(lora_status_t s) {
     case LORA_ERR_WORKSPACE: return "workspace too small or misaligned";
     case LORA_ERR_PAGE: return "invalid pool geometry";
     case LORA_ERR_HIP: return "HIP runtime error";
-    case LORA_ERR_UNSUPPORTED: return "not implemented in this build";
+    case LORA_ERR_UNSUPPORTED: return "not implemented by this library";
   }
   return "unknown status";
 }

@@ -230,8 +230,8 @@ __device__ __forceinline__ void shrink_blocks(const LoraArgs &a, const Item &it,
 // grid (item, slice or all slices, k split).  PER_SLICE: one slice per
 // workgroup, at most 4 rank blocks (ranks <= 64), so only the 4-block path
 // is compiled and it alone sets the register budget (64-row items: 422 ->
-// 212 VGPRs, two waves per SIMD; with one k step per round the 8192-row
-// prefill shrink went 31.4 -> 23.4 us, 2 or 4 steps per round 24.8 / 25.2 us).
+// 212 VGPRs, two waves per SIMD; with one k step per load round the
+// 8192-row prefill shrink went 31.4 -> 23.4 us, 2 or 4 steps 24.8 / 25.2 us).
 constexpr int kShrinkSteps64 = 1;
 template <int RB, bool PER_SLICE>
 __global__ __launch_bounds__(256) void k_shrink_mfma(LoraArgs a) {
