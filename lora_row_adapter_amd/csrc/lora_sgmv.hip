@@ -311,10 +311,14 @@ __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int keep) {
 // 16.2 us at the 70B q+v shapes).  The shrink keeps its masked loads: it is
 // bound by the address path of the vector memory unit, where clamped lanes
 // cost as much as real ones (measured slower with clamping).
-template <int RB, int ECB, bool FAST>
+// RMX: the largest padded rank the instantiation takes (32 or RMAX_MFMA).
+// The plan drops rows whose rank exceeds max_rank, so every item's rank is
+// at most the slices' largest max_rank, which selects RMX on the host: at
+// ranks up to 32 the B fragments and registers of the second k step go.
+template <int RB, int ECB, bool FAST, int RMX>
 __device__ __forceinline__ void expand_body(const LoraArgs &a) {
   constexpr int RBK = RB / 16;
-  constexpr int KP = RMAX_MFMA + 8;  // padded LDS row (bf16)
+  constexpr int KP = RMX + 8;  // padded LDS row (bf16)
   constexpr int CB = ECB / 64;       // 16-column blocks per wave
   constexpr int CPR = ECB / 8;       // 16-byte y chunks per row
   constexpr int CPT = 16 * CPR / 256;  // 16-byte y chunks per thread per 16-row pass
@@ -369,9 +373,9 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
   const AdapterRef &ar = sl.ar;
   const int stride = ar.pooled ? r : ar.max_rank;  // B row stride (elements)
   const bool bvec = (stride % 8) == 0;
-  bf16x8_t fb[RMAX_MFMA / 32][CB];
+  bf16x8_t fb[RMX / 32][CB];
 #pragma unroll
-  for (int ks = 0; ks < RMAX_MFMA / 32; ++ks) {
+  for (int ks = 0; ks < RMX / 32; ++ks) {
     const int jl = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -506,7 +510,7 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < RMAX_MFMA / 32; ++ks) {
+  for (int ks = 0; ks < RMX / 32; ++ks) {
     if (ks * 32 >= kp) break;
     const int jl = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
@@ -562,17 +566,36 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
 // 16-row items (decode batches).  (Capping its registers so that 4-6
 // workgroups fit per CU instead of 3 measured no faster at 4 and twice as
 // slow at 5-6, where it spills.)
-template <int ECB, bool FAST>
+template <bool FAST, int RMX>
 __global__ __launch_bounds__(256) void k_expand_mfma16(LoraArgs a) {
-  expand_body<16, ECB, FAST>(a);
+  expand_body<16, kExpandCols16, FAST, RMX>(a);
 }
 // 64-row items (prefill runs): three waves per SIMD (168 VGPRs) instead of
 // two (228): prefill expand 47.1 -> 44.9 us, though the fast variant spills
 // a few registers
-template <bool FAST>
+template <bool FAST, int RMX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_expand_mfma64(
     LoraArgs a) {
-  expand_body<64, 256, FAST>(a);
+  expand_body<64, 256, FAST, RMX>(a);
+}
+
+template <int RB, bool FAST, int RMX>
+void expand_launch(const LoraArgs &a, dim3 grid, hipStream_t st) {
+  if constexpr (RB == 16)
+    hipLaunchKernelGGL((k_expand_mfma16<FAST, RMX>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_expand_mfma64<FAST, RMX>), grid, dim3(256), 0, st, a);
+}
+
+template <int RB>
+void expand_pick(const LoraArgs &a, bool fast, bool r32, dim3 grid, hipStream_t st) {
+  if (fast) {
+    if (r32) expand_launch<RB, true, 32>(a, grid, st);
+    else expand_launch<RB, true, RMAX_MFMA>(a, grid, st);
+  } else {
+    if (r32) expand_launch<RB, false, 32>(a, grid, st);
+    else expand_launch<RB, false, RMAX_MFMA>(a, grid, st);
+  }
 }
 
 }  // namespace
@@ -605,15 +628,12 @@ hipError_t launch_expand_sgmv(const LoraArgs &a0, int rows_per_item, hipStream_t
   for (int q = 0; q < a.n_slices; ++q)
     fast = fast && !a.sl[q].ar.pooled && a.sl[q].ar.max_rank % 8 == 0 && a.sl[q].d % 8 == 0 &&
            a.sl[q].col0 % 8 == 0;
-  if (rows_per_item == 16) {
-    const dim3 grid((unsigned)(a.L.items_g_cap * cb8));
-    if (fast) hipLaunchKernelGGL((k_expand_mfma16<kExpandCols16, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_expand_mfma16<kExpandCols16, false>), grid, dim3(256), 0, st, a);
-  } else {
-    const dim3 grid((unsigned)(a.L.items_s_cap * cb8));
-    if (fast) hipLaunchKernelGGL((k_expand_mfma64<true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_expand_mfma64<false>), grid, dim3(256), 0, st, a);
-  }
+  bool r32 = true;
+  for (int q = 0; q < a.n_slices; ++q) r32 = r32 && a.sl[q].ar.max_rank <= 32;
+  if (rows_per_item == 16)
+    expand_pick<16>(a, fast, r32, dim3((unsigned)(a.L.items_g_cap * cb8)), st);
+  else
+    expand_pick<64>(a, fast, r32, dim3((unsigned)(a.L.items_s_cap * cb8)), st);
   return hipGetLastError();
 }
 
