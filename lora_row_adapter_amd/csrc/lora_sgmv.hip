@@ -301,9 +301,11 @@ __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int keep) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-// FAST: every slice in slots with max_rank % 8 == 0 (16-byte B rows), y
-// 16-byte aligned with every slice's columns a multiple of 8 wide and at a
-// multiple of 8.  Then the B fragments, the item's row numbers, the y runs
+// FAST: y 16-byte aligned with every slice's columns a multiple of 8 wide
+// and at a multiple of 8, and either every slice in slots with max_rank % 8
+// == 0 (16-byte B rows) or (POOL) every slice in a pool, where an item whose
+// rank is a multiple of 8 takes the same B loads through the page table.
+// Then the B fragments, the item's row numbers, the y runs
 // and the k-split partials are all loaded unconditionally at clamped
 // addresses and masked by selects afterwards, so they leave back to back
 // (loads under a branch -- even a uniform one -- or behind a slot/pool
@@ -315,7 +317,7 @@ __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int keep) {
 // The plan drops rows whose rank exceeds max_rank, so every item's rank is
 // at most the slices' largest max_rank, which selects RMX on the host: at
 // ranks up to 32 the B fragments and registers of the second k step go.
-template <int RB, int ECB, bool FAST, int RMX>
+template <int RB, int ECB, bool FAST, int RMX, bool POOL>
 __device__ __forceinline__ void expand_body(const LoraArgs &a) {
   constexpr int RBK = RB / 16;
   constexpr int KP = RMX + 8;  // padded LDS row (bf16)
@@ -374,47 +376,70 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
   const int stride = ar.pooled ? r : ar.max_rank;  // B row stride (elements)
   const bool bvec = (stride % 8) == 0;
   bf16x8_t fb[RMX / 32][CB];
+  // pooled B rows are r elements long: the vector loads need r % 8 == 0
+  // (the pool base is 16-byte aligned and a page at least 256 bytes, so a
+  // vector never straddles pages); other ranks take the generic loads
+  const bool fast_b = FAST && (!POOL || (r & 7) == 0);
+  if (fast_b) {
 #pragma unroll
-  for (int ks = 0; ks < RMX / 32; ++ks) {
-    const int jl = ks * 32 + (lane >> 4) * 8;
+    for (int ks = 0; ks < RMX / 32; ++ks) {
+      const int jl = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int64_t n = n0 + (wave * CB + cb) * 16 + (lane & 15);
-      if constexpr (FAST) {
-        // a rank chunk past the rank loads chunk 0's vector (same lines)
+      for (int cb = 0; cb < CB; ++cb) {
+        const int64_t n = n0 + (wave * CB + cb) * 16 + (lane & 15);
+        // a rank chunk past the rank loads chunk 0's vector (same lines);
+        // the clamped (na, ja) is always inside the adapter's B
         const bool ok = ks * 32 < kp && n < sl.d && jl < r;
         const bool ok0 = n < sl.d && jl - ks * 32 < r;
         const int64_t na = ok || ok0 ? n : n0;
         const int ja = ok ? jl : (ok0 ? jl - ks * 32 : 0);
-        const bf16x8_t v = ld16(ar.B + (((int64_t)it.adapter * ar.d + na) * ar.max_rank + ja) * 2);
-        fb[ks][cb] = keep_first(v, ok ? r - jl : 0);
-        continue;
-      }
-      bf16x8_t v = zero8();
-      if (ks * 32 < kp && n < sl.d && jl < r) {
-        if (bvec && jl + 8 <= r) {
-          v = ld16(adapter_b_ptr(ar, it.adapter, r, n, jl));
-        } else if (bvec && !ar.pooled) {
-          // a slot row is padded to max_rank (a multiple of 8): load the
-          // whole 8-rank vector and zero the ranks past r (padding may hold
-          // anything)
-          uint16_t e8[8];
-          *reinterpret_cast<bf16x8_t *>(e8) = ld16(adapter_b_ptr(ar, it.adapter, r, n, jl));
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (jl + q >= r) e8[q] = 0;
-          v = __builtin_bit_cast(bf16x8_t, e8);
+        const uint8_t *bp;
+        if constexpr (POOL) {
+          // every page-table entry is loaded unconditionally, so the
+          // compiler issues them as one batch ahead of the B vectors
+          const int64_t off = ((int64_t)r * ar.k + na * r + ja) * 2;
+          const int64_t page =
+              ar.page_table[(int64_t)it.adapter * ar.max_pages + (off >> ar.page_shift)];
+          bp = ar.pool + (page << ar.page_shift) + (off & (ar.page_bytes - 1));
         } else {
-          uint16_t e8[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            e8[q] = (jl + q < r) ? *reinterpret_cast<const uint16_t *>(
-                                       adapter_b_ptr(ar, it.adapter, r, n, jl + q))
-                                 : (uint16_t)0;
-          v = __builtin_bit_cast(bf16x8_t, e8);
+          bp = ar.B + (((int64_t)it.adapter * ar.d + na) * ar.max_rank + ja) * 2;
         }
+        fb[ks][cb] = keep_first(ld16(bp), ok ? r - jl : 0);
       }
-      fb[ks][cb] = v;
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < RMX / 32; ++ks) {
+      const int jl = ks * 32 + (lane >> 4) * 8;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int64_t n = n0 + (wave * CB + cb) * 16 + (lane & 15);
+        bf16x8_t v = zero8();
+        if (ks * 32 < kp && n < sl.d && jl < r) {
+          if (bvec && jl + 8 <= r) {
+            v = ld16(adapter_b_ptr(ar, it.adapter, r, n, jl));
+          } else if (bvec && !ar.pooled) {
+            // a slot row is padded to max_rank (a multiple of 8): load the
+            // whole 8-rank vector and zero the ranks past r (padding may
+            // hold anything)
+            uint16_t e8[8];
+            *reinterpret_cast<bf16x8_t *>(e8) = ld16(adapter_b_ptr(ar, it.adapter, r, n, jl));
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (jl + q >= r) e8[q] = 0;
+            v = __builtin_bit_cast(bf16x8_t, e8);
+          } else {
+            uint16_t e8[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              e8[q] = (jl + q < r) ? *reinterpret_cast<const uint16_t *>(
+                                         adapter_b_ptr(ar, it.adapter, r, n, jl + q))
+                                   : (uint16_t)0;
+            v = __builtin_bit_cast(bf16x8_t, e8);
+          }
+        }
+        fb[ks][cb] = v;
+      }
     }
   }
   const bool yvec = a.y_vec && (sl.col0 % 8) == 0;
@@ -566,36 +591,38 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
 // 16-row items (decode batches).  (Capping its registers so that 4-6
 // workgroups fit per CU instead of 3 measured no faster at 4 and twice as
 // slow at 5-6, where it spills.)
-template <bool FAST, int RMX>
+template <bool FAST, int RMX, bool POOL>
 __global__ __launch_bounds__(256) void k_expand_mfma16(LoraArgs a) {
-  expand_body<16, kExpandCols16, FAST, RMX>(a);
+  expand_body<16, kExpandCols16, FAST, RMX, POOL>(a);
 }
 // 64-row items (prefill runs): three waves per SIMD (168 VGPRs) instead of
 // two (228): prefill expand 47.1 -> 44.9 us, though the fast variant spills
 // a few registers
-template <bool FAST, int RMX>
+template <bool FAST, int RMX, bool POOL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_expand_mfma64(
     LoraArgs a) {
-  expand_body<64, 256, FAST, RMX>(a);
+  expand_body<64, 256, FAST, RMX, POOL>(a);
 }
 
-template <int RB, bool FAST, int RMX>
+template <int RB, bool FAST, int RMX, bool POOL>
 void expand_launch(const LoraArgs &a, dim3 grid, hipStream_t st) {
   if constexpr (RB == 16)
-    hipLaunchKernelGGL((k_expand_mfma16<FAST, RMX>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_expand_mfma16<FAST, RMX, POOL>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_expand_mfma64<FAST, RMX>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_expand_mfma64<FAST, RMX, POOL>), grid, dim3(256), 0, st, a);
+}
+
+template <int RB, int RMX>
+void expand_mode(const LoraArgs &a, int mode, dim3 grid, hipStream_t st) {
+  if (mode == 1) expand_launch<RB, true, RMX, false>(a, grid, st);
+  else if (mode == 2) expand_launch<RB, true, RMX, true>(a, grid, st);
+  else expand_launch<RB, false, RMX, false>(a, grid, st);
 }
 
 template <int RB>
-void expand_pick(const LoraArgs &a, bool fast, bool r32, dim3 grid, hipStream_t st) {
-  if (fast) {
-    if (r32) expand_launch<RB, true, 32>(a, grid, st);
-    else expand_launch<RB, true, RMAX_MFMA>(a, grid, st);
-  } else {
-    if (r32) expand_launch<RB, false, 32>(a, grid, st);
-    else expand_launch<RB, false, RMAX_MFMA>(a, grid, st);
-  }
+void expand_pick(const LoraArgs &a, int mode, bool r32, dim3 grid, hipStream_t st) {
+  if (r32) expand_mode<RB, 32>(a, mode, grid, st);
+  else expand_mode<RB, RMAX_MFMA>(a, mode, grid, st);
 }
 
 }  // namespace
@@ -624,16 +651,20 @@ hipError_t launch_expand_sgmv(const LoraArgs &a0, int rows_per_item, hipStream_t
     a.col_blk[q + 1] = a.col_blk[q] + (int32_t)((a.sl[q].d + ecb - 1) / ecb);
   // one dimension: item-major, column blocks padded to a multiple of 8
   const int64_t cb8 = ((int64_t)a.col_blk[a.n_slices] + 7) / 8 * 8;
-  bool fast = a.y_vec != 0;
-  for (int q = 0; q < a.n_slices; ++q)
-    fast = fast && !a.sl[q].ar.pooled && a.sl[q].ar.max_rank % 8 == 0 && a.sl[q].d % 8 == 0 &&
-           a.sl[q].col0 % 8 == 0;
+  // mode 1: fast loads, slots; 2: fast loads, every slice in a pool; 0: generic
+  bool yfast = a.y_vec != 0, slots8 = true, pooled = true;
+  for (int q = 0; q < a.n_slices; ++q) {
+    yfast = yfast && a.sl[q].d % 8 == 0 && a.sl[q].col0 % 8 == 0;
+    slots8 = slots8 && !a.sl[q].ar.pooled && a.sl[q].ar.max_rank % 8 == 0;
+    pooled = pooled && a.sl[q].ar.pooled;
+  }
+  const int mode = !yfast ? 0 : slots8 ? 1 : pooled ? 2 : 0;
   bool r32 = true;
   for (int q = 0; q < a.n_slices; ++q) r32 = r32 && a.sl[q].ar.max_rank <= 32;
   if (rows_per_item == 16)
-    expand_pick<16>(a, fast, r32, dim3((unsigned)(a.L.items_g_cap * cb8)), st);
+    expand_pick<16>(a, mode, r32, dim3((unsigned)(a.L.items_g_cap * cb8)), st);
   else
-    expand_pick<64>(a, fast, r32, dim3((unsigned)(a.L.items_s_cap * cb8)), st);
+    expand_pick<64>(a, mode, r32, dim3((unsigned)(a.L.items_s_cap * cb8)), st);
   return hipGetLastError();
 }
 

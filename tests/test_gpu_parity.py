@@ -400,7 +400,13 @@ def test_paths_small(oracle_mod, pname, path):
                       (wl.custom(seed=41, M=300, k=264, d=130, ranks=[1, 3, 8, 17, 33, 64],
                                  max_rank=64), False),
                       (wl.custom(seed=42, M=1500, k=512, d=96, ranks=[8, 40, 16], max_rank=40,
-                                 sorted_ids=True), False)):
+                                 sorted_ids=True), False),
+                      # pooled: ranks that are and are not multiples of 8, 16- and
+                      # 64-row items
+                      (wl.custom(seed=43, M=300, k=264, d=136, ranks=[1, 3, 8, 17, 32, 64],
+                                 max_rank=64), True),
+                      (wl.custom(seed=44, M=1500, k=512, d=96, ranks=[8, 40, 16], max_rank=40,
+                                 sorted_ids=True), True)):
         _check_full(oracle_mod, DevWorkload(w, w.projections[0], pooled=pooled),
                     "%s %s" % (w.name, pname), path=path)
 
