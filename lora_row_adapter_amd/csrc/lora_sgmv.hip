@@ -73,6 +73,21 @@ __device__ __forceinline__ ARow make_arow(const AdapterRef &ar, int s, int64_t j
   return w;
 }
 
+// A pooled row whose bytes for k in [kbeg, kend) lie in one page becomes a
+// slot-style row (base + 2 kk): one page-table load per lane before the k
+// loop instead of one ahead of every vector.  (k and the bounds are
+// multiples of 8, so the last vector ends at byte 2 kend - 1.)
+__device__ __forceinline__ void arow_resolve(ARow &w, int64_t kbeg, int64_t kend) {
+  if (w.pt == nullptr || kend <= kbeg) return;
+  const int64_t o0 = w.off + kbeg * 2;
+  const int64_t idx = o0 >> w.shift;
+  if (idx != ((w.off + kend * 2 - 1) >> w.shift)) return;
+  const int64_t pg = w.pt[idx];
+  w.base = reinterpret_cast<const uint8_t *>(reinterpret_cast<uintptr_t>(w.base) +
+                                             (pg - idx) * (int64_t(1) << w.shift) + w.off);
+  w.pt = nullptr;
+}
+
 __device__ __forceinline__ const uint8_t *arow_ptr(const ARow &w, int64_t kk) {
   if (w.pt == nullptr) return w.base + kk * 2;
   const int64_t off = w.off + kk * 2;
@@ -163,6 +178,7 @@ __device__ __forceinline__ void shrink_blocks(const LoraArgs &a, const Item &it,
       const int j = jb * 16 + (lane & 15);
       jv[g] = j < r;
       arow[g] = make_arow(a.sl[slice].ar, it.adapter, jv[g] ? j : 0);
+      arow_resolve(arow[g], kbeg, kend);
     }
   }
 
