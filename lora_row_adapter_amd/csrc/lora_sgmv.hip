@@ -399,6 +399,9 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
   if (fast_b) {
 #pragma unroll
     for (int ks = 0; ks < RMX / 32; ++ks) {
+      // uniform: no rank chunk left (the MFMA loop stops at the same step,
+      // so the fragments past it are never read)
+      if (ks > 0 && ks * 32 >= kp) break;
       const int jl = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
