@@ -598,7 +598,16 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
       for (int q = 0; q < 8; ++q) e8[q] = f32_to_bf16_bits(bf16_bits_to_f32(old[q]) + scale * sv[q]);
       const int64_t n = n0 + col;
       if (FAST || (yvec && n + 8 <= sl.d)) {
-        *reinterpret_cast<uint4 *>(yp[c]) = __builtin_bit_cast(uint4, e8);
+        if constexpr (RB == 64) {
+          // prefill runs: y is far larger than L2 and each run is written
+          // once, so the stores stream past it (nontemporal: 42.1 -> 37.9 us
+          // at 8192 x 4096)
+          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, e8),
+                                      reinterpret_cast<u32x4_t *>(yp[c]));
+        } else {
+          *reinterpret_cast<uint4 *>(yp[c]) = __builtin_bit_cast(uint4, e8);
+        }
       } else {
         for (int q = 0; q < 8; ++q)
           if (n + q < sl.d) yp[c][q] = e8[q];
