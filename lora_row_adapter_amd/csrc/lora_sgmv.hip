@@ -481,7 +481,14 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
       const int64_t n = n0 + (ch % CPR) * 8;
       const bool ok = row < nr && n < sl.d;
       uint16_t *p = yb + (int64_t)rows[c] * a.ldy + (ok ? n : n0);
-      yv[c] = *reinterpret_cast<const uint4 *>(p);
+      if constexpr (RB == 64) {
+        // prefill runs: read once, then overwritten by a streaming store
+        // (nontemporal: 37.6 -> 35.8 us at 8192 x 4096)
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        yv[c] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p)));
+      } else {
+        yv[c] = *reinterpret_cast<const uint4 *>(p);
+      }
       yp[c] = ok ? p : nullptr;
     }
   }
