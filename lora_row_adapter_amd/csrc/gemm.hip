@@ -650,7 +650,15 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       const uint16_t *src = ct + row * CLD + c * 8;
       uint16_t *dst = p.y + (int64_t)gm * p.ldy + gn;
       if (p.vec_store && gn + 8 <= p.N) {
-        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+        if constexpr (BM == 256 && BN == 256) {
+          // the largest tiles run at prefill sizes, where y is far larger
+          // than L2: the stores stream past it
+          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(src),
+                                      reinterpret_cast<u32x4_t *>(dst));
+        } else {
+          *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+        }
       } else {
         for (int e = 0; e < 8 && gn + e < p.N; ++e) dst[e] = src[e];
       }
