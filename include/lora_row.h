@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 2
+#define LORA_ABI_VERSION 3
 
 typedef enum lora_status {
   LORA_OK = 0,
@@ -328,7 +328,10 @@ lora_status_t lora_merge(lora_dtype_t dtype, int64_t d, int64_t k, const void *W
                          float coef, void *W_out, int64_t ldo, void *stream);
 
 /*
- * Page-table translation as the kernels do it, exported for bit-exact checks:
+ * Page-table translation as the kernels do it ("S-LoRA: what the paper
+ * actually says ...", "Unified paging": an adapter's weights sit in
+ * fixed-size blocks of one pool, located through that adapter's block
+ * list), exported for bit-exact checks:
  * phys_off[i] = page_table[adapter[i]][logical_off[i] / page_bytes] * page_bytes
  *               + logical_off[i] % page_bytes,
  * or -1 when adapter[i] is outside [0, n_adapters), the logical page is past
@@ -340,13 +343,36 @@ lora_status_t lora_translate(const lora_adapters_t *adapters, const int32_t *ada
                              void *stream);
 
 /*
- * Synchronises `stream` and reads the error counters of the last plan run in
- * this workspace: rows with an id outside [-1, n_adapters), rows whose
- * adapter rank is outside [0, max_rank], rows whose adapter pages are
- * missing or outside the pool.  Output pointers are HOST and may be NULL.
+ * Device-side error report of a workspace.  The per-row counts follow the
+ * readings of "LoRA Adapters: Many Models in One", "The model runner's part"
+ * (a per-token slot index, or none) and "S-LoRA: ...", "Unified paging" (an
+ * adapter's blocks found through its page list): a row whose id, rank or
+ * pages cannot be used is served as a row without adapter and counted.
+ *
+ * Synchronises `stream`, then reads:
+ *   n_bad_ids, n_bad_ranks, n_bad_pages -- counts of the last plan run in
+ *     this workspace: rows with an id outside [-1, n_adapters), rows whose
+ *     adapter rank is outside [0, max_rank], rows whose adapter pages are
+ *     missing or outside the pool;
+ *   n_sync_expired -- split-K workgroup pairs of the base GEMM whose second
+ *     half stopped waiting for the first half's partial (a bounded wait of
+ *     ~0.3 s; that output tile is wrong).  Cumulative since the workspace
+ *     was zero-filled: lora_linear* count it at word 8 of the workspace,
+ *     lora_gemm at word 8 of its own workspace.  Zero-fill a workspace once
+ *     when allocating it for this count to mean anything; 0 in normal runs.
+ * Output pointers are HOST and may be NULL.
  */
 lora_status_t lora_check(const void *workspace, void *stream, int64_t *n_bad_ids,
-                         int64_t *n_bad_ranks, int64_t *n_bad_pages);
+                         int64_t *n_bad_ranks, int64_t *n_bad_pages, int64_t *n_sync_expired);
+
+/*
+ * Testing hook for the error path of the split-K pairs (no page defines
+ * it).  Sets the bound, in polls, of the second workgroup's wait in later
+ * launches; 0 makes every such wait expire at once (wrong tiles, counted as
+ * n_sync_expired, every workgroup exits normally); a negative value restores
+ * the default.  Process-wide; not for production use.
+ */
+lora_status_t lora_test_sync_spin_limit(int32_t polls);
 
 /*
  * Per-kernel GPU timing.  While enabled, every kernel that lora_linear /

@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     Adapters, QWeight, W_INT4, W_INT8, lora_gemm_q, lora_linear_sliced_q,
     LoraError, Profiler, Slice, abi_version, library_path, load_library, lora_check, lora_gemm,
     lora_linear, lora_linear_sliced, lora_merge, lora_plan, lora_plan_view, lora_translate, new_workspace,
-    status_str, workspace_bytes, workspace_bytes_sliced, gemm_workspace_bytes,
+    status_str, workspace_bytes, workspace_bytes_sliced, gemm_workspace_bytes, test_sync_spin_limit,
 )

@@ -164,8 +164,11 @@ def load_library():
     lib.lora_merge.restype = i32
     lib.lora_translate.argtypes = [pad, p, p, i64, p, p]
     lib.lora_translate.restype = i32
-    lib.lora_check.argtypes = [p, p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.lora_check.argtypes = [p, p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                               ctypes.POINTER(i64)]
     lib.lora_check.restype = i32
+    lib.lora_test_sync_spin_limit.argtypes = [i32]
+    lib.lora_test_sync_spin_limit.restype = i32
     lib.lora_profile_enable.argtypes = [i32]
     lib.lora_profile_enable.restype = i32
     lib.lora_profile_read.argtypes = [ctypes.POINTER(_CProfile), i32]
@@ -488,7 +491,8 @@ def workspace_bytes(max_rows: int, d: int, k: int, dtype: torch.dtype, adapters:
 def new_workspace(max_rows: int, d: int, k: int, dtype: torch.dtype, adapters: Adapters,
                   device=None) -> torch.Tensor:
     n = workspace_bytes(max_rows, d, k, dtype, adapters)
-    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    # zero-filled once: the library's sticky error words start at 0
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
 
 
 def gemm_workspace_bytes(M: int, k: int, d: int, dtype: torch.dtype) -> int:
@@ -511,7 +515,7 @@ def lora_gemm(x: torch.Tensor, W: torch.Tensor, y: Optional[torch.Tensor] = None
     if workspace is None:
         n = gemm_workspace_bytes(x.shape[0], x.shape[1], W.shape[0], x.dtype)
         if n > 0:
-            workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+            workspace = torch.zeros(n, dtype=torch.uint8, device=x.device)
     wsp, wsn = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
     _check(lib.lora_gemm(_dtype_code(x), x.shape[0], x.shape[1], W.shape[0], xp, ldx, wp, ldw,
                          yp, ldy, wsp, wsn, _stream_ptr(stream)), "lora_gemm")
@@ -563,7 +567,7 @@ def lora_linear_sliced(x: torch.Tensor, W: torch.Tensor, slices, adapter_ids: to
     if y is None:
         y = torch.empty((M, d_total), dtype=x.dtype, device=x.device)
     if workspace is None:
-        workspace = torch.empty(workspace_bytes_sliced(M, k, x.dtype, slices), dtype=torch.uint8,
+        workspace = torch.zeros(workspace_bytes_sliced(M, k, x.dtype, slices), dtype=torch.uint8,
                                 device=x.device)
     xp, ldx = _rows(x, "x")
     wp, ldw = _rows(W, "W")
@@ -668,7 +672,7 @@ def lora_linear_sliced_q(x: torch.Tensor, W: QWeight, slices, adapter_ids: torch
     if y is None:
         y = torch.empty((M, d_total), dtype=x.dtype, device=x.device)
     if workspace is None:
-        workspace = torch.empty(workspace_bytes_sliced(M, k, x.dtype, slices), dtype=torch.uint8,
+        workspace = torch.zeros(workspace_bytes_sliced(M, k, x.dtype, slices), dtype=torch.uint8,
                                 device=x.device)
     xp, ldx = _rows(x, "x")
     yp, ldy = _rows(y, "y")
@@ -715,11 +719,19 @@ def lora_translate(adapters: Adapters, adapter: torch.Tensor, logical_off: torch
 
 
 def lora_check(workspace: torch.Tensor, stream=None) -> dict:
+    """Device error counters of a workspace (synchronises the stream)."""
     lib = load_library()
-    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    a, b, c, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     _check(lib.lora_check(_dev(workspace, "workspace"), _stream_ptr(stream), ctypes.byref(a),
-                          ctypes.byref(b), ctypes.byref(c)), "lora_check")
-    return {"n_bad_ids": a.value, "n_bad_ranks": b.value, "n_bad_pages": c.value}
+                          ctypes.byref(b), ctypes.byref(c), ctypes.byref(e)), "lora_check")
+    return {"n_bad_ids": a.value, "n_bad_ranks": b.value, "n_bad_pages": c.value,
+            "n_sync_expired": e.value}
+
+
+def test_sync_spin_limit(polls: int) -> None:
+    """Testing hook: bound of the split-K pairs' wait (0: every wait expires,
+    counted; negative: the default)."""
+    _check(load_library().lora_test_sync_spin_limit(int(polls)), "lora_test_sync_spin_limit")
 
 
 class Profiler:

@@ -28,6 +28,10 @@ enum HdrWord {
   kHdrItemsGather = 5,
   kHdrItemsSgmv = 6,
   kHdrRows = 7,
+  // Split-K pairs of the base GEMM whose second workgroup stopped waiting for
+  // the first one's partial (bounded wait; the tile is then wrong).  Sticky:
+  // the plan never writes it, the GEMM only adds to it.
+  kHdrSyncExpired = 8,
   kHdrWords = 64
 };
 

@@ -170,10 +170,13 @@ struct PipeArgs {
   int vec_store;  // y rows 16-byte aligned (ldy % 8 == 0, aligned base)
   FusedT ft;      // TX kernels only
   // split-K pairs (SK == 2): fp32 partial tiles, per pair an arrival word
-  // and a ready flag, and this launch's epoch
+  // and a ready flag, this launch's epoch (never 0), the bound of the
+  // second workgroup's wait (polls) and the counter of expired waits
   float *part;
   uint64_t *sync;
   uint64_t epoch;
+  int32_t spin_limit;
+  int32_t *expired;
 };
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -496,10 +499,14 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
     // second adds the first one's fp32 partial and runs the epilogue; the
     // first writes its partial, raises the pair's ready flag and leaves.
     // Arrival order comes from swapping this launch's epoch into the pair's
-    // arrival word (any other value there means "first"), so no word needs
-    // clearing between calls; only the second waits, and only for a
-    // workgroup that has already arrived.  a + b == b + a in fp32, so the
-    // result does not depend on which half arrives first.
+    // arrival word (any other value there means "first"); only the second
+    // waits, and only for a workgroup that has already arrived.  The second
+    // puts both words back to 0 once it has seen them (no other workgroup
+    // touches them again in this launch), so a later launch that carries the
+    // same epoch -- a replayed graph -- finds the pair as if new.  Its wait
+    // is bounded; an expired wait (the tile then holds a stale partial) is
+    // counted in *expired, which lora_check reports.  a + b == b + a in
+    // fp32, so the result does not depend on which half arrives first.
     // Every access to the partial, the flag and the arrival word is
     // device-scope (sc1: coherent across the XCDs' L2s by itself, as the
     // compiler emits relaxed agent-scope atomics), and the writer waits for
@@ -514,9 +521,12 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
     const __amdgpu_buffer_rsrc_t part = part_rsrc(part_base);
     __shared__ int s_second;
     __syncthreads();  // every wave is past its k loop
-    if (tid == 0)  // relaxed: the partial is published through the ready flag
-      s_second = __hip_atomic_exchange(arrive, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 p.epoch;
+    if (tid == 0) {  // relaxed: the partial is published through the ready flag
+      const bool second =
+          __hip_atomic_exchange(arrive, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.epoch;
+      if (second) __hip_atomic_store(arrive, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_second = second;
+    }
     __syncthreads();
     if (!s_second) {
       if (!producer) {
@@ -536,10 +546,18 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
     if (tid == 0) {
       // bounded: the first half has arrived, so its flag follows its
       // partial within microseconds
-      for (int n = 0; n < (1 << 22); ++n) {
-        if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.epoch) break;
+      bool seen = false;
+      for (int n = 0; n < p.spin_limit; ++n) {
+        if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.epoch) {
+          seen = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
       }
+      if (seen)
+        __hip_atomic_store(ready, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        __hip_atomic_fetch_add(p.expired, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     part_in = part_base;
@@ -803,9 +821,14 @@ constexpr size_t kSplitPartBytes = (size_t)8 * 2 * 10 * 64 * 16;  // per pair (t
 int64_t split_pairs(int64_t M, int64_t d) {
   return ((M + kSplitBM - 1) / kSplitBM) * ((d + kSplitBN - 1) / kSplitBN);
 }
+// GEMM region: a 256-byte header (word kHdrSyncExpired counts expired pair
+// waits when the region is a lora_gemm workspace), the pairs' partial
+// slots, then their arrival / ready words
+constexpr size_t kGemmHdrBytes = 256;
 size_t split_bytes(int64_t M, int64_t d) {
   const int64_t P = split_pairs(M, d);
-  return ((size_t)P * kSplitPartBytes + 255) / 256 * 256 + ((size_t)P * 16 + 255) / 256 * 256;
+  return kGemmHdrBytes + ((size_t)P * kSplitPartBytes + 255) / 256 * 256 +
+         ((size_t)P * 16 + 255) / 256 * 256;
 }
 bool split_ok(int64_t M, int64_t k, int64_t d, void *gws, size_t gws_bytes) {
   // k >= 256: each half holds at least two k-tiles
@@ -813,16 +836,23 @@ bool split_ok(int64_t M, int64_t k, int64_t d, void *gws, size_t gws_bytes) {
          gws_bytes >= split_bytes(M, d);
 }
 std::atomic<uint64_t> g_epoch{0x9E3779B97F4A7C15ull};
+constexpr int32_t kSpinDefault = 1 << 22;  // polls of ~2 x 64 clocks: ~0.3 s
+std::atomic<int32_t> g_spin_limit{kSpinDefault};
 template <bool TX>
-void launch_split(PipeArgs pa, int64_t M, int64_t d, void *gws, hipStream_t st) {
+void launch_split(PipeArgs pa, int64_t M, int64_t d, void *gws, int32_t *expired, hipStream_t st) {
   const int64_t P = split_pairs(M, d);
   pa.tiles_m = (int)((M + kSplitBM - 1) / kSplitBM);
   pa.tiles_n = (int)((d + kSplitBN - 1) / kSplitBN);
   static_assert(kSplitBN == 144, "split-K pairs use 256 x 144 tiles");
-  pa.part = reinterpret_cast<float *>(gws);
-  pa.sync = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(gws) +
+  uint8_t *region = reinterpret_cast<uint8_t *>(gws);
+  pa.part = reinterpret_cast<float *>(region + kGemmHdrBytes);
+  pa.sync = reinterpret_cast<uint64_t *>(region + kGemmHdrBytes +
                                          ((size_t)P * kSplitPartBytes + 255) / 256 * 256);
+  pa.expired = expired ? expired : reinterpret_cast<int32_t *>(region) + kHdrSyncExpired;
+  pa.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  // 0 is the "nobody arrived" value of the pair words
   pa.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
+  if (pa.epoch == 0) pa.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
   hipLaunchKernelGGL((k_gemm_bf16_split<144, TX, 2>), dim3(pa.tiles_m * pa.tiles_n * 2), dim3(768),
                      0, st, pa);
 }
@@ -842,9 +872,13 @@ size_t gemm_ws_bytes(int64_t M, int64_t k, int64_t d) {
   return split_bytes(M, d);
 }
 
+void set_sync_spin_limit(int32_t polls) {
+  g_spin_limit.store(polls < 0 ? kSpinDefault : polls, std::memory_order_relaxed);
+}
+
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, void *gws,
-                       size_t gws_bytes, hipStream_t st) {
+                       size_t gws_bytes, hipStream_t st, int32_t *expired) {
   if (M <= 0 || d <= 0) return hipSuccess;
   if (dtype == 1) {
     if (pipe_ok(k, ldx, ldw)) {
@@ -854,7 +888,7 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
         case 1: launch_pipe<256, 128, 4, 1, 3>(pa, st); break;
         case 2:
           if (split_ok(M, k, d, gws, gws_bytes)) {
-            launch_split<false>(pa, M, d, gws, st);
+            launch_split<false>(pa, M, d, gws, expired, st);
           } else {
             launch_pipe<128, 144, 4, 1, 3>(pa, st);
           }
@@ -932,14 +966,14 @@ bool gemm_footprint(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx,
 
 hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                              const void *W, int64_t ldw, void *y, int64_t ldy, const FusedT &ft,
-                             void *gws, size_t gws_bytes, hipStream_t st) {
+                             void *gws, size_t gws_bytes, hipStream_t st, int32_t *expired) {
   if (ft.cap <= 0 || ft.cap != gemm_fused_cap(M, k, d, ldx, ldw) ||
       ft.n_slices * ft.S > kFusedMaxEntries || ft.S > 256 || ft.n_slices > kMaxSlices)
     return hipErrorInvalidValue;
   PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
   pa.ft = ft;
   if (split_ok(M, k, d, gws, gws_bytes)) {
-    launch_split<true>(pa, M, d, gws, st);
+    launch_split<true>(pa, M, d, gws, expired, st);
   } else {
     launch_pipe<128, 144, 4, 1, 3, true>(pa, st);
   }

@@ -119,9 +119,14 @@ constexpr int kFusedMaxEntries = 256;  // n_slices * S the fused path scans
 // GEMM's region of the workspace (split-K partials), 256-byte aligned, or
 // nullptr; shapes with gemm_ws_bytes(M, k, d) > 0 run split-K pairs when it
 // holds that many bytes, else the unsplit tiles (another summation order).
+// expired: where split-K pairs count expired waits (nullptr: word
+// kHdrSyncExpired of the GEMM region's own 256-byte header).
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, void *gws,
-                       size_t gws_bytes, hipStream_t st);
+                       size_t gws_bytes, hipStream_t st, int32_t *expired = nullptr);
+// Bound of the split-K pairs' wait in polls for later launches (< 0: the
+// default); a test hook that makes every wait expire at once with 0.
+void set_sync_spin_limit(int32_t polls);
 // Bytes of GEMM workspace the split-K launch of this shape uses (0: none).
 size_t gemm_ws_bytes(int64_t M, int64_t k, int64_t d);
 // Capacity (t_all columns) a fused launch of this shape would have; 0 when
@@ -130,7 +135,8 @@ int32_t gemm_fused_cap(int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw
 // The base GEMM with the shrink folded in (ft.cap == gemm_fused_cap(...)).
 hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                              const void *W, int64_t ldw, void *y, int64_t ldy, const FusedT &ft,
-                             void *gws, size_t gws_bytes, hipStream_t st);
+                             void *gws, size_t gws_bytes, hipStream_t st,
+                             int32_t *expired = nullptr);
 // Base GEMM with a quantized weight (bf16 x and y).
 struct QGemmArgs {
   int32_t fmt;  // 1 INT8 (per-row scales), 2 INT4 (per-row, per-k-group scales)

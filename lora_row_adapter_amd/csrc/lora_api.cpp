@@ -624,9 +624,14 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
     }
     hipError_t e = timed(LORA_K_GEMM, st, [&] {
       if (qw) return launch_gemm_q(make_q_args(qw, Mc, k, d_total, xc, ldx, yc, ldy), st);
+      // expired split-K waits are counted in the plan header, where
+      // lora_check reads them
+      int32_t *expired = reinterpret_cast<int32_t *>(ws + L.hdr) + kHdrSyncExpired;
       if (fcap > 0)
-        return launch_gemm_fused(Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, ft, gws, gws_bytes, st);
-      return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, gws, gws_bytes, st);
+        return launch_gemm_fused(Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, ft, gws, gws_bytes, st,
+                                 expired);
+      return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, gws, gws_bytes, st,
+                         expired);
     });
     if (e != hipSuccess) return LORA_ERR_HIP;
     if (fork && hipStreamWaitEvent(st, ev_join, 0) != hipSuccess) return LORA_ERR_HIP;
@@ -736,9 +741,9 @@ lora_status_t lora_translate(const lora_adapters_t *adapters, const int32_t *ada
 }
 
 lora_status_t lora_check(const void *workspace, void *stream, int64_t *n_bad_ids,
-                         int64_t *n_bad_ranks, int64_t *n_bad_pages) {
+                         int64_t *n_bad_ranks, int64_t *n_bad_pages, int64_t *n_sync_expired) {
   if (workspace == nullptr) return LORA_ERR_ARG;
-  int32_t h[3] = {0, 0, 0};
+  int32_t h[kHdrSyncExpired + 1] = {};
   hipStream_t st = (hipStream_t)stream;
   if (hipMemcpyAsync(h, workspace, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess)
     return LORA_ERR_HIP;
@@ -746,6 +751,12 @@ lora_status_t lora_check(const void *workspace, void *stream, int64_t *n_bad_ids
   if (n_bad_ids) *n_bad_ids = h[kHdrBadIds];
   if (n_bad_ranks) *n_bad_ranks = h[kHdrBadRanks];
   if (n_bad_pages) *n_bad_pages = h[kHdrBadPages];
+  if (n_sync_expired) *n_sync_expired = h[kHdrSyncExpired];
+  return LORA_OK;
+}
+
+lora_status_t lora_test_sync_spin_limit(int32_t polls) {
+  set_sync_spin_limit(polls);
   return LORA_OK;
 }
 

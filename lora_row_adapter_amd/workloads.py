@@ -112,7 +112,10 @@ def _build(name: str, index: int, dtype: torch.dtype, M: int, k: int, proj_dims:
     rx, rw, ra, rb, rs = _rng_streams(index, 5)
     ranks = np.asarray(ranks, np.int32)
     alphas = np.asarray(alphas, np.float32)
-    scales = (alphas / ranks.astype(np.float32)).astype(np.float32)
+    # alpha / r with the true rank; an adapter of rank 0 adds nothing and
+    # gets scale 0 (no division by zero)
+    scales = np.where(ranks > 0, alphas / np.maximum(ranks, 1).astype(np.float32),
+                      np.float32(0)).astype(np.float32)
     ids, seq = ids_fn(rs)
     x = _normal(rx, (M, k), 1.0, dtype)
     projections = []

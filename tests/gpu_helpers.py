@@ -1,5 +1,6 @@
 """Glue for the GPU tests: move seeded workloads to the device, call the
 library through its binding, and compare with the oracle."""
+import hashlib
 import sys
 
 import numpy as np
@@ -56,9 +57,49 @@ class DevWorkload:
         return out
 
 
-def oracle_rows(oracle, w, proj, rows=None, ids=None):
-    """fp64 oracle output for the given rows (all rows when None)."""
+_ORACLE_CACHE = {}
+_ORACLE_CACHE_MAX = 8
+
+
+def _digest(*arrays) -> str:
+    h = hashlib.sha256()
+    for a in arrays:
+        if hasattr(a, "detach"):
+            a = a.detach().cpu().contiguous()
+            a = a.view(torch.int16) if a.dtype == torch.bfloat16 else a
+            a = a.numpy()
+        a = np.ascontiguousarray(a)
+        h.update(str(a.dtype).encode() + str(a.shape).encode())
+        h.update(a.tobytes())
+    return h.hexdigest()
+
+
+def oracle_full(oracle, w, proj, ids=None, x=None):
+    """fp64 oracle output for every row, memoised on the exact inputs (a
+    digest of x, W, every A and B, the scales and the ids), so the large
+    workloads are computed once per session however many tests compare
+    against them."""
+    ids = w.ids if ids is None else np.asarray(ids, np.int32)
+    x = w.x if x is None else x
+    key = _digest(x, proj.W, w.scales, ids, np.asarray([w.max_rank]),
+                  *[a for a in proj.A], *[b for b in proj.B])
+    hit = _ORACLE_CACHE.get(key)
+    if hit is None:
+        hit = oracle.lora_linear(x, proj.W, proj.A, proj.B, w.scales.astype(np.float64), ids,
+                                 max_rank=w.max_rank)
+        if len(_ORACLE_CACHE) >= _ORACLE_CACHE_MAX:
+            _ORACLE_CACHE.pop(next(iter(_ORACLE_CACHE)))
+        _ORACLE_CACHE[key] = hit
+    return hit
+
+
+def oracle_rows(oracle, w, proj, rows=None, ids=None, cache=False):
+    """fp64 oracle output for the given rows (all rows when None).  With
+    cache=True every row is computed once (oracle_full) and indexed."""
     ids = w.ids if ids is None else ids
+    if cache:
+        full = oracle_full(oracle, w, proj, ids=ids)
+        return full if rows is None else full[np.asarray(rows)]
     if rows is None:
         return oracle.lora_linear(w.x, proj.W, proj.A, proj.B, w.scales.astype(np.float64), ids,
                                   max_rank=w.max_rank)
@@ -67,17 +108,10 @@ def oracle_rows(oracle, w, proj, rows=None, ids=None):
                               w.scales.astype(np.float64), ids[rows], max_rank=w.max_rank)
 
 
-def sample_rows(w, n: int, seed: int = 0) -> np.ndarray:
-    """Rows to check at full size: both ends, every segment boundary region,
-    none rows, and a seeded random remainder."""
-    rng = np.random.default_rng(seed)
-    M = w.M
-    pick = {0, M - 1, M // 2}
-    none = np.flatnonzero(w.ids < 0)
-    pick.update(none[:4].tolist())
-    change = np.flatnonzero(np.diff(w.ids) != 0)
-    pick.update(change[:8].tolist())
-    pick.update((change[:8] + 1).tolist())
-    while len(pick) < min(n, M):
-        pick.add(int(rng.integers(0, M)))
-    return np.array(sorted(pick), dtype=np.int64)
+def assert_covers_present_adapters(w, rows=None) -> None:
+    """Every adapter some row uses has at least one row among those compared."""
+    ids = np.asarray(w.ids)
+    present = set(np.unique(ids[ids >= 0]).tolist())
+    seen = present if rows is None else set(np.unique(ids[np.asarray(rows)]).tolist())
+    missing = sorted(present - seen)
+    assert not missing, "adapters never compared with the oracle: %s" % missing[:20]

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lr.abi_version() == 2
+    assert lr.abi_version() == 3
     assert lr.status_str(0) == "ok"
     assert "workspace" in lr.status_str(5)
 
@@ -112,7 +112,7 @@ def test_gemm_and_misc_reject_bad_arguments_on_host():
     assert lib.lora_gemm(1, 0, 64, 64, 0, 64, 0, 64, 0, 64, None, 0, None) == 0
     # a misaligned workspace is refused before any launch
     assert lib.lora_gemm(1, 4, 64, 64, 256, 64, 512, 64, 1024, 64, 4096 + 16, 1 << 20, None) == 5
-    assert lib.lora_check(None, None, None, None, None) == 1
+    assert lib.lora_check(None, None, None, None, None, None) == 1
     c = _slots_struct()
     assert lib.lora_translate(ctypes.byref(c), 16, 16, 4, 16, None) == 1   # slots have no pages
     v = B._CPlanView()
@@ -133,17 +133,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 def test_gemm_workspace_sizes():
     """Split-K pairs (256 x 144 tiles, two k halves) at shapes that would run
-    128 x 144 tiles with more than 128 rows: per pair 8 waves x 2 x 10 MFMA
-    blocks of 64 lanes x 16 bytes, plus 16 bytes of arrival/ready words, each
-    region 256-byte aligned."""
+    128 x 144 tiles with more than 128 rows: a 256-byte header (the expired
+    wait counter), per pair 8 waves x 2 x 10 MFMA blocks of 64 lanes x 16
+    bytes, plus 16 bytes of arrival/ready words, each region 256-byte
+    aligned."""
     bf16 = 1
     pairs = 2 * 64  # 512 rows, d = 9216
     part = pairs * 8 * 2 * 10 * 64 * 16
-    assert lr.gemm_workspace_bytes(512, 8192, 9216, torch.bfloat16) == part + 2048
+    assert lr.gemm_workspace_bytes(512, 8192, 9216, torch.bfloat16) == 256 + part + 2048
     assert lr.gemm_workspace_bytes(128, 8192, 9216, torch.bfloat16) == 0   # one row tile
     assert lr.gemm_workspace_bytes(512, 8192, 4096, torch.bfloat16) == 0   # not a 144-column shape
     assert lr.gemm_workspace_bytes(512, 8192, 9216, torch.float32) == 0
-    assert lr.gemm_workspace_bytes(400, 8192, 9216, torch.bfloat16) == part + 2048  # ragged rows
+    assert lr.gemm_workspace_bytes(400, 8192, 9216, torch.bfloat16) == 256 + part + 2048  # ragged rows
     assert lr.gemm_workspace_bytes(384, 8192, 9216, torch.bfloat16) == 0  # 128 x 128 tiles fit one round
     lib = lr.load_library()
     assert lib.lora_gemm_workspace_bytes(512, 8192 + 64, 9216, bf16) == 0  # k halves not 64-aligned

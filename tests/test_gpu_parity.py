@@ -11,7 +11,7 @@ import torch
 
 import lora_row_adapter_amd as lr
 from lora_row_adapter_amd import workloads as wl
-from gpu_helpers import DevWorkload, TOL, normwise, oracle_rows, sample_rows, say
+from gpu_helpers import DevWorkload, TOL, assert_covers_present_adapters, normwise, oracle_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,8 @@ def _plan_case(oracle_mod, ids, S, ranks, R, pooled=None):
     for key in ("n_bad_ids", "n_bad_ranks", "n_bad_pages"):
         assert got[key] == ref[key], key
     chk = lr.lora_check(ws)
-    assert chk == {k_: ref[k_] for k_ in ("n_bad_ids", "n_bad_ranks", "n_bad_pages")}
+    assert chk == {**{k_: ref[k_] for k_ in ("n_bad_ids", "n_bad_ranks", "n_bad_pages")},
+                   "n_sync_expired": 0}
     # work items cover every adapted row exactly once
     assert got["items_gather"] == sum((l + 15) // 16 for l in ref["seg_len"])
     assert got["items_sgmv"] == sum((l + 63) // 64 for l in ref["seg_len"])
@@ -194,14 +195,19 @@ def test_translate_bit_exact(oracle_mod):
 # the layer: full workloads (small ones whole, large ones on sampled rows)
 # ---------------------------------------------------------------------------
 
-def _check_full(oracle_mod, dw: DevWorkload, label: str, rows=None, path=lr.PATH_AUTO):
+def _check_full(oracle_mod, dw: DevWorkload, label: str, rows=None, path=lr.PATH_AUTO,
+                cache=False):
+    """Every row (rows=None) or the given rows against the oracle; cache=True
+    memoises the oracle's full output for the large seeded workloads."""
     w, p = dw.w, dw.p
-    say("layer %s (%s, M=%d k=%d d=%d)" % (label, w.name, w.M, w.k, p.d))
+    say("layer %s (%s, M=%d k=%d d=%d, %s rows)" % (label, w.name, w.M, w.k, p.d,
+                                                   "all" if rows is None else len(rows)))
+    assert_covers_present_adapters(w, rows)
     y = dw.run(path=path).double().cpu().numpy()
     base = lr.lora_gemm(dw.x, dw.W)
     torch.cuda.synchronize()
     base = base.double().cpu().numpy()
-    ref = oracle_rows(oracle_mod, w, p, rows)
+    ref = oracle_rows(oracle_mod, w, p, rows, cache=cache)
     got = y if rows is None else y[rows]
     err = normwise(got, ref)
     say("  normwise error %.3g" % err)
@@ -213,7 +219,7 @@ def _check_full(oracle_mod, dw: DevWorkload, label: str, rows=None, path=lr.PATH
     ids = w.ids if rows is None else w.ids[rows]
     adapted = ids >= 0
     if adapted.any():
-        ref_base = oracle_rows(oracle_mod, w, p, rows, ids=np.full(w.M, -1, np.int32))
+        ref_base = oracle_rows(oracle_mod, w, p, rows, ids=np.full(w.M, -1, np.int32), cache=cache)
         d_got = (got - (base if rows is None else base[rows]))[adapted]
         d_ref = (ref - ref_base)[adapted]
         derr = normwise(d_got, d_ref)
@@ -247,9 +253,13 @@ def test_c1_decode(oracle_mod):
     _check_full(oracle_mod, DevWorkload(w, w.projections[0]), "c1")
 
 
-def test_c2_prefill(oracle_mod):
-    w = wl.c2_prefill_bf16()
-    _check_full(oracle_mod, DevWorkload(w, w.projections[0]), "c2", rows=sample_rows(w, 48))
+@pytest.fixture(scope="module")
+def c2():
+    return wl.c2_prefill_bf16()
+
+
+def test_c2_prefill(oracle_mod, c2):
+    _check_full(oracle_mod, DevWorkload(c2, c2.projections[0]), "c2", cache=True)
 
 
 @pytest.fixture(scope="module")
@@ -259,7 +269,7 @@ def c3():
 
 @pytest.mark.parametrize("proj", ["q", "v"])
 def test_c3_proj70b(oracle_mod, c3, proj):
-    _check_full(oracle_mod, DevWorkload(c3, c3.proj(proj)), "c3 " + proj, rows=sample_rows(c3, 40))
+    _check_full(oracle_mod, DevWorkload(c3, c3.proj(proj)), "c3 " + proj, cache=True)
 
 
 @pytest.fixture(scope="module")
@@ -269,10 +279,28 @@ def c4():
 
 def test_c4_paged(oracle_mod, c4):
     p = c4.projections[0]
-    rows = sample_rows(c4, 40)
-    y_pool = _check_full(oracle_mod, DevWorkload(c4, p, pooled=True), "c4 pool 2MiB", rows=rows)
+    y_pool = _check_full(oracle_mod, DevWorkload(c4, p, pooled=True), "c4 pool 2MiB", cache=True)
     y_slot = DevWorkload(c4, p).run().double().cpu().numpy()
     assert np.array_equal(y_pool, y_slot)
+
+
+@pytest.mark.parametrize("pname,path", [("gather", lr.PATH_GATHER), ("sgmv", lr.PATH_SGMV)],
+                         ids=["gather", "sgmv"])
+def test_u2_pages_at_c4_shape(oracle_mod, c4, pname, path):
+    """Page crossing at the paged-pool shape ("S-LoRA: ...", "Unified
+    paging"): d = k = 5120, rank 16, 4 KiB pages, so each adapter's 320 KiB
+    [A | B] spans 80 pages at seeded physical positions (spare pool pages
+    hold NaN).  Every row against the oracle, and bitwise equal to the same
+    path over 2 MiB pages (one page per adapter): only addresses differ."""
+    p = c4.projections[0]
+    small = DevWorkload(c4, p, pooled=True, page_bytes=4096)
+    assert int(small.table.shape[1]) == 80
+    y4k = _check_full(oracle_mod, small, "u2 at c4 shape, 4 KiB pages " + pname, path=path,
+                      cache=True)
+    del small
+    big = DevWorkload(c4, p, pooled=True)
+    y2m = big.run(path=path).double().cpu().numpy()
+    assert np.array_equal(y4k, y2m)
 
 
 # ---------------------------------------------------------------------------
@@ -355,10 +383,8 @@ def test_row_chunks_beyond_plan_limit(oracle_mod):
     dw = DevWorkload(w, w.projections[0])
     say("row chunks M=%d" % w.M)
     y = dw.run().double().cpu().numpy()
-    rows = sample_rows(w, 64, seed=1)
-    rows = np.union1d(rows, np.arange(8180, 8210))
-    ref = oracle_rows(oracle_mod, w, w.projections[0], rows)
-    assert normwise(y[rows], ref) <= 2e-2
+    ref = oracle_rows(oracle_mod, w, w.projections[0])   # every row, both chunks
+    assert normwise(y, ref) <= 2e-2
 
 
 # ---------------------------------------------------------------------------
@@ -375,22 +401,28 @@ def test_paths_c1(oracle_mod, pname, path):
 
 
 @pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
-def test_paths_c2(oracle_mod, pname, path):
-    w = wl.c2_prefill_bf16()
-    _check_full(oracle_mod, DevWorkload(w, w.projections[0]), "c2 " + pname,
-                rows=sample_rows(w, 48), path=path)
+def test_paths_c2(oracle_mod, c2, pname, path):
+    _check_full(oracle_mod, DevWorkload(c2, c2.projections[0]), "c2 " + pname, path=path,
+                cache=True)
 
 
+@pytest.mark.parametrize("proj", ["q", "v"])
 @pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
-def test_paths_c3(oracle_mod, c3, pname, path):
-    _check_full(oracle_mod, DevWorkload(c3, c3.proj("q")), "c3 q " + pname,
-                rows=sample_rows(c3, 40), path=path)
+def test_paths_c3(oracle_mod, c3, pname, path, proj):
+    _check_full(oracle_mod, DevWorkload(c3, c3.proj(proj)), "c3 %s %s" % (proj, pname), path=path,
+                cache=True)
 
 
 @pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
 def test_paths_c4_pool(oracle_mod, c4, pname, path):
     _check_full(oracle_mod, DevWorkload(c4, c4.projections[0], pooled=True), "c4 pool " + pname,
-                rows=sample_rows(c4, 40), path=path)
+                path=path, cache=True)
+
+
+@pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
+def test_paths_c4_slots(oracle_mod, c4, pname, path):
+    _check_full(oracle_mod, DevWorkload(c4, c4.projections[0]), "c4 slots " + pname, path=path,
+                cache=True)
 
 
 @pytest.mark.parametrize("pname,path", PATHS, ids=[p[0] for p in PATHS])
@@ -446,12 +478,11 @@ def test_sliced_c3_q_and_v(oracle_mod, c3, pname, path):
     torch.cuda.synchronize()
     base = lr.lora_gemm(dq.x, W)
     torch.cuda.synchronize()
-    rows = sample_rows(c3, 40)
     yq = y[:, :pq.d].double().cpu().numpy()
     yv = y[:, pq.d:].double().cpu().numpy()
     for name, got, p in (("q", yq, pq), ("v", yv, pv)):
-        ref = oracle_rows(oracle_mod, c3, p, rows)
-        err = normwise(got[rows], ref)
+        ref = oracle_rows(oracle_mod, c3, p, cache=True)   # every row, every adapter
+        err = normwise(got, ref)
         say("  %s normwise error %.3g" % (name, err))
         assert err <= 2e-2
     none = np.flatnonzero(c3.ids < 0)

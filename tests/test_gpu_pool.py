@@ -198,7 +198,7 @@ def test_managed_pool_linear_matches_slots(oracle_mod):
         y = lr.lora_linear(slots.x, slots.W, ad, slots.ids, slots.scales, workspace=ws, path=path)
         torch.cuda.synchronize()
         chk = lr.lora_check(ws)
-        assert chk == {"n_bad_ids": 0, "n_bad_ranks": 0, "n_bad_pages": 0}
+        assert chk == {"n_bad_ids": 0, "n_bad_ranks": 0, "n_bad_pages": 0, "n_sync_expired": 0}
         y_slot = slots.run(path=path)
         assert torch.equal(y, y_slot), path
         assert normwise(y.double().cpu().numpy(), ref) <= 2e-2
@@ -216,7 +216,7 @@ def test_evicted_adapter_rows_get_the_base(oracle_mod):
     y = lr.lora_linear(slots.x, slots.W, ad, slots.ids, slots.scales, workspace=ws)
     chk = lr.lora_check(ws)
     n2 = int((w.ids == 2).sum())
-    assert chk == {"n_bad_ids": 0, "n_bad_ranks": n2, "n_bad_pages": 0}
+    assert chk == {"n_bad_ids": 0, "n_bad_ranks": n2, "n_bad_pages": 0, "n_sync_expired": 0}
     base = lr.lora_gemm(slots.x, slots.W)
     y_slot = slots.run()
     torch.cuda.synchronize()
