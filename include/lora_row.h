@@ -234,6 +234,35 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
                                  int32_t path, uint32_t flags, void *stream);
 
 /*
+ * lora_linear_sliced without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP-graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and results as
+ * lora_linear_sliced (bitwise: the same kernels run), except:
+ *   - the plan regions, shrink partials and the base GEMM's split-K partials
+ *     live in a static device array of LORA_NOALLOC_SCRATCH_BYTES that the
+ *     library holds on every GPU it runs on until the process ends; a call
+ *     whose workspace need (lora_workspace_bytes_sliced) exceeds it returns
+ *     LORA_ERR_WORKSPACE and launches nothing;
+ *   - the call allocates nothing (no hipMalloc / hipFree, no stream or event
+ *     creation): the plan runs on `stream` ahead of the base GEMM, not beside
+ *     it, and launches are not timed by lora_profile_*;
+ *   - every call on one GPU shares that GPU's array and its contents stay
+ *     from the last call: calls that overlap on one GPU (two streams, two
+ *     threads) race, so the caller serialises them; LORA_FLAG_REUSE_PLAN
+ *     reuses the last plan made in the array;
+ *   - the device error counters it keeps are not reported (use
+ *     lora_linear_sliced with a workspace and lora_check to read them).
+ * The first call on a device looks up the array's device address there
+ * (make that call outside any graph capture).
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lora_status_t lora_linear_sliced_noalloc(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
+                                         int64_t ldx, const void *W, int64_t ldw,
+                                         int32_t n_slices, const lora_slice_t *slices,
+                                         const int32_t *adapter_ids, void *y, int64_t ldy,
+                                         int32_t path, uint32_t flags, void *stream);
+
+/*
  * Quantized base weight (bf16 activations and adapters; the base GEMM
  * dequantizes on the fly).  "Your LoRA Adapters Are Thrashing Your GPUs",
  * section 02: production deployments quantize the base model to INT4 or INT8

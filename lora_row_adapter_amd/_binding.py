@@ -150,6 +150,9 @@ def load_library():
     lib.lora_linear_sliced.argtypes = [i32, i64, i64, p, i64, p, i64, i32, psl, p, p, i64, p, sz,
                                        i32, u32, p]
     lib.lora_linear_sliced.restype = i32
+    lib.lora_linear_sliced_noalloc.argtypes = [i32, i64, i64, p, i64, p, i64, i32, psl, p, p, i64,
+                                               i32, u32, p]
+    lib.lora_linear_sliced_noalloc.restype = i32
     lib.lora_plan.argtypes = [i64, i64, i64, i32, pad, p, p, sz, p]
     lib.lora_plan.restype = i32
     lib.lora_plan_view.argtypes = [p, sz, i64, pad, ctypes.POINTER(_CPlanView)]
@@ -583,6 +586,35 @@ def lora_linear_sliced(x: torch.Tensor, W: torch.Tensor, slices, adapter_ids: to
                                 int(flags), _stream_ptr(stream))
     _check(st, "lora_linear_sliced")
     return y
+
+
+def lora_linear_sliced_noalloc(x: torch.Tensor, W: torch.Tensor, slices, adapter_ids: torch.Tensor,
+                               y: torch.Tensor, path: int = PATH_AUTO, flags: int = 0,
+                               stream=None) -> torch.Tensor:
+    """lora_linear_sliced without a workspace: the library's static per-GPU
+    scratch array (LORA_NOALLOC_SCRATCH_BYTES) stands in for it and the call
+    allocates nothing.  y is the caller's [M, sum d_i] output."""
+    lib = load_library()
+    M, k = x.shape
+    d_total = sum(sl.d for sl in slices)
+    if W.shape[0] != d_total:
+        raise ValueError("W must stack the slices' weights: %d rows expected" % d_total)
+    xp, ldx = _rows(x, "x")
+    wp, ldw = _rows(W, "W")
+    yp, ldy = _rows(y, "y")
+    if W.dtype != x.dtype or y.dtype != x.dtype:
+        raise TypeError("x, W, y must share a dtype")
+    if adapter_ids.numel() != M or y.shape[0] != M:
+        raise ValueError("adapter_ids and y must have one entry per row")
+    arr = _slice_array(slices)
+    st = lib.lora_linear_sliced_noalloc(_dtype_code(x), M, k, xp, ldx, wp, ldw, len(slices), arr,
+                                        _dev(adapter_ids, "adapter_ids", torch.int32), yp, ldy,
+                                        int(path), int(flags), _stream_ptr(stream))
+    _check(st, "lora_linear_sliced_noalloc")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LORA_NOALLOC_SCRATCH_BYTES
 
 
 def lora_plan(adapter_ids: torch.Tensor, adapters: Adapters, k: int, d: int, dtype: torch.dtype,

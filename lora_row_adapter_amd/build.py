@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblora_row.so")
 SOURCES = ["lora_api.cpp", "plan.hip", "gemm.hip", "lora_gather.hip", "lora_sgmv.hip",
-           "pool.hip", "pool_mgr.cpp", "merge.hip", "gemm_q.hip"]
+           "pool.hip", "pool_mgr.cpp", "merge.hip", "gemm_q.hip", "noalloc.hip"]
 ARCH = os.environ.get("LORA_ROW_ARCH", "gfx950")
 
 

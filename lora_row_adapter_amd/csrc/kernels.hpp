@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/lora_row.h"
 #include "common.hpp"
 
 namespace lora {
@@ -221,5 +222,15 @@ hipError_t launch_merge(const MergeArgs &m, hipStream_t st);
 hipError_t launch_pool_fill(int32_t *p, int64_t n, int32_t v, hipStream_t st);
 hipError_t launch_pool_rows(const PoolRowsArgs &a, hipStream_t st);
 hipError_t launch_pool_pull(const PoolPullArgs &a, hipStream_t st);
+
+// The multi-slice layer behind lora_linear_sliced(_q) (the C ABI's types;
+// defined in lora_api.cpp).  self_contained: create no library resource --
+// the plan runs on the caller's stream and no launch is timed.
+lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
+                                 int64_t ldx, const void *W, int64_t ldw, const lora_qweight_t *qw,
+                                 int32_t n_slices, const lora_slice_t *slices,
+                                 const int32_t *adapter_ids, void *y, int64_t ldy, void *workspace,
+                                 size_t workspace_bytes, int32_t path, uint32_t flags, void *stream,
+                                 bool self_contained);
 
 }  // namespace lora

@@ -147,6 +147,11 @@ static hipError_t timed(int c, hipStream_t st, F &&launch) {
   prof::end(slot, st);
   return e;
 }
+// timed() unless the call must not create the profiler's events
+template <typename F>
+static hipError_t maybe_timed(bool untimed, int c, hipStream_t st, F &&launch) {
+  return untimed ? launch() : timed(c, st, launch);
+}
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -400,9 +405,9 @@ static PlanArgs make_plan_args(int64_t M, int64_t k, lora_dtype_t dtype, int32_t
 static lora_status_t run_plan(int64_t M, int64_t k, lora_dtype_t dtype, int32_t n_slices,
                               const lora_slice_t *slices, const int32_t *ids, uint8_t *ws,
                               const WsLayout &L, hipStream_t st,
-                              size_t max_lds = kPlanLdsBeside) {
+                              size_t max_lds = kPlanLdsBeside, bool untimed = false) {
   const PlanArgs p = make_plan_args(M, k, dtype, n_slices, slices, ids, ws, L);
-  hipError_t e = timed(LORA_K_PLAN, st, [&] { return launch_plan(p, st, max_lds); });
+  hipError_t e = maybe_timed(untimed, LORA_K_PLAN, st, [&] { return launch_plan(p, st, max_lds); });
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -453,15 +458,19 @@ lora_status_t lora_plan_view(const void *workspace, size_t workspace_bytes, int6
   return LORA_OK;
 }
 
+}  // extern "C"
+
+namespace lora {
 // The layer over several slices; the base weight is dense (W, ldw) or, with
-// qw != nullptr, quantized (bf16 only).
-static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
-                                        int64_t ldx, const void *W, int64_t ldw,
-                                        const lora_qweight_t *qw, int32_t n_slices,
-                                        const lora_slice_t *slices, const int32_t *adapter_ids,
-                                        void *y, int64_t ldy, void *workspace,
-                                        size_t workspace_bytes, int32_t path, uint32_t flags,
-                                        void *stream) {
+// qw != nullptr, quantized (bf16 only).  self_contained: use no library
+// resource that may need creating -- the plan runs on the caller's stream
+// (no side stream or fork/join events) and no launch is timed.
+lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
+                                 int64_t ldx, const void *W, int64_t ldw, const lora_qweight_t *qw,
+                                 int32_t n_slices, const lora_slice_t *slices,
+                                 const int32_t *adapter_ids, void *y, int64_t ldy, void *workspace,
+                                 size_t workspace_bytes, int32_t path, uint32_t flags, void *stream,
+                                 bool self_contained) {
   int32_t S = 0, R = 0;
   int64_t d_total = 0;
   if (slices == nullptr || n_slices < 1 || n_slices > LORA_MAX_SLICES) return LORA_ERR_ARG;
@@ -603,26 +612,26 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
     hipStream_t ps = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     const bool reuse = (flags & LORA_FLAG_REUSE_PLAN) != 0;
-    bool beside = true;
-    if (!reuse && !qw) {
+    bool beside = !self_contained;
+    if (!reuse && !qw && beside) {
       KernelFootprint pf, gf;
       const PlanArgs pa = make_plan_args(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L);
       beside = plan_footprint(pa, &pf) &&
                gemm_footprint(dtype, Mc, k, d_total, ldx, ldw, gws, gws_bytes, fcap > 0, &gf) &&
                fits_beside(gf, pf);
     }
-    const bool fork = !reuse && beside && side::get(&ps, &ev_fork, &ev_join);
+    const bool fork = !reuse && beside && !self_contained && side::get(&ps, &ev_fork, &ev_join);
     if (!reuse) {
       if (fork) {
         if (hipEventRecord(ev_fork, st) != hipSuccess || hipStreamWaitEvent(ps, ev_fork, 0) != hipSuccess)
           return LORA_ERR_HIP;
       }
       s = run_plan(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L, fork ? ps : st,
-                   fork || beside ? kPlanLdsBeside : kPlanLdsAlone);
+                   fork || beside ? kPlanLdsBeside : kPlanLdsAlone, self_contained);
       if (s != LORA_OK) return s;
       if (fork && hipEventRecord(ev_join, ps) != hipSuccess) return LORA_ERR_HIP;
     }
-    hipError_t e = timed(LORA_K_GEMM, st, [&] {
+    hipError_t e = maybe_timed(self_contained, LORA_K_GEMM, st, [&] {
       if (qw) return launch_gemm_q(make_q_args(qw, Mc, k, d_total, xc, ldx, yc, ldy), st);
       // expired split-K waits are counted in the plan header, where
       // lora_check reads them
@@ -638,20 +647,24 @@ static lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k
 
     if (use_mfma) {
       if (fcap == 0) {  // else the base GEMM computed t
-        e = timed(LORA_K_SGMV_SHRINK, st, [&] { return launch_shrink_sgmv(a, rpi, per_slice, st); });
+        e = maybe_timed(self_contained, LORA_K_SGMV_SHRINK, st, [&] { return launch_shrink_sgmv(a, rpi, per_slice, st); });
         if (e != hipSuccess) return LORA_ERR_HIP;
       }
-      e = timed(LORA_K_SGMV_EXPAND, st, [&] { return launch_expand_sgmv(a, rpi, st); });
+      e = maybe_timed(self_contained, LORA_K_SGMV_EXPAND, st, [&] { return launch_expand_sgmv(a, rpi, st); });
       if (e != hipSuccess) return LORA_ERR_HIP;
     } else {
-      e = timed(LORA_K_SHRINK, st, [&] { return launch_shrink_gather(a, st); });
+      e = maybe_timed(self_contained, LORA_K_SHRINK, st, [&] { return launch_shrink_gather(a, st); });
       if (e != hipSuccess) return LORA_ERR_HIP;
-      e = timed(LORA_K_EXPAND, st, [&] { return launch_expand_gather(a, st); });
+      e = maybe_timed(self_contained, LORA_K_EXPAND, st, [&] { return launch_expand_gather(a, st); });
       if (e != hipSuccess) return LORA_ERR_HIP;
     }
   }
   return LORA_OK;
 }
+
+}  // namespace lora
+
+extern "C" {
 
 lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const void *x,
                                  int64_t ldx, const void *W, int64_t ldw, int32_t n_slices,
@@ -659,7 +672,7 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
                                  int64_t ldy, void *workspace, size_t workspace_bytes,
                                  int32_t path, uint32_t flags, void *stream) {
   return linear_sliced_impl(dtype, M, k, x, ldx, W, ldw, nullptr, n_slices, slices, adapter_ids,
-                            y, ldy, workspace, workspace_bytes, path, flags, stream);
+                            y, ldy, workspace, workspace_bytes, path, flags, stream, false);
 }
 
 lora_status_t lora_linear_sliced_q(int64_t M, int64_t k, const void *x, int64_t ldx,
@@ -669,7 +682,8 @@ lora_status_t lora_linear_sliced_q(int64_t M, int64_t k, const void *x, int64_t 
                                    int32_t path, uint32_t flags, void *stream) {
   if (W == nullptr) return LORA_ERR_ARG;
   return linear_sliced_impl(LORA_DTYPE_BF16, M, k, x, ldx, nullptr, 0, W, n_slices, slices,
-                            adapter_ids, y, ldy, workspace, workspace_bytes, path, flags, stream);
+                            adapter_ids, y, ldy, workspace, workspace_bytes, path, flags, stream,
+                            false);
 }
 
 lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
