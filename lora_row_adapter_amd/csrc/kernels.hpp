@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/lora_row.h"
+#include "lora_row.h"
 #include "common.hpp"
 
 namespace lora {

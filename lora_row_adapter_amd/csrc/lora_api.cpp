@@ -9,7 +9,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/lora_row.h"
+#include "lora_row.h"
 #include "kernels.hpp"
 
 namespace lora {

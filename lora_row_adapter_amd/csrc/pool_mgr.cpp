@@ -27,7 +27,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/lora_pool.h"
+#include "lora_pool.h"
 #include "kernels.hpp"
 
 namespace {
