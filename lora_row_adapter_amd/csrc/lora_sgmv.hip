@@ -623,6 +623,188 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
   }
 }
 
+// Decode expand on independent waves (16-row items).  Each wave updates one
+// item's 16 rows over NU units of 64 columns of one slice with no LDS and no
+// barrier: it computes the transposed product D' = B_s t^T on the matrix
+// cores -- B_s rows (ranks contiguous) as the A operand, t rows as the B
+// operand -- with the B_s rows permuted so that D' lands in the registers
+// as whole y runs: A-operand row m of column block cb is column 16 (m / 4)
+// + 4 cb + m % 4 of the unit's 64, so lane l ends up with y row l % 16,
+// columns 16 (l / 16) .. + 15, after the four blocks (MFMA 16x16x32 D
+// layout: lane l holds rows 4 (l / 16) + i of column l % 16).  It then
+// reads those 32 bytes of y, adds scale * D' and writes them back.  t is
+// split into bf16 hi + lo parts (two MFMAs per block), as in expand_body,
+// and serves all NU units; every load of the wave is issued before its
+// first MFMA (a wave's life is a few dependent memory round trips: kernel
+// arguments and item header ~1.2 us, then its data, measured at the 70B
+// q+v shape with per-wave s_memrealtime stamps).
+// Needs: 16-byte aligned y with every slice's columns a multiple of 16 wide
+// at a multiple of 8, the partials' row width a multiple of 8, and slots
+// whose max_rank is a multiple of 8 or (POOL) every slice in a pool.
+// 64-column units per wave.  One: the waves are co-resident and wait on
+// memory, so more of them in flight beats more loads per wave (4 units at
+// the 70B q+v shape: 14.3 -> 22.7 us); 80 VGPRs give six waves per SIMD.
+constexpr int kW16Units = 1;
+constexpr int kW16Cols = 4 * 64 * kW16Units;    // columns per workgroup
+template <int RMX, bool POOL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void k_expand_w16(LoraArgs a) {
+  constexpr int NU = kW16Units;
+  const int ncb = a.col_blk[a.n_slices];  // kW16Cols-column blocks over all slices
+  const int per_xcd = (ncb + 7) >> 3;
+  const int b = blockIdx.x;
+  const int q = b >> 3;
+  const int item = q / per_xcd;
+  const int xcd = b & 7;
+  const int cbk = ((xcd * ncb) >> 3) + (q - item * per_xcd);
+  if (cbk >= (((xcd + 1) * ncb) >> 3)) return;
+  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
+  const Item it = reinterpret_cast<const Item *>(a.ws + a.L.items_g)[item];
+  const ItemRows *ix = reinterpret_cast<const ItemRows *>(a.ws + a.L.items_gx) + item;
+  if (item >= hdr[kHdrItemsGather]) return;
+  int slice = 0;
+  while (slice + 1 < a.n_slices && cbk >= a.col_blk[slice + 1]) ++slice;
+  const SliceRef &sl = a.sl[slice];
+  const int r = ix->r[slice];
+  if (r == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // the wave's columns: NU units of 64 starting at nw
+  const int64_t nw = (int64_t)(cbk - a.col_blk[slice]) * kW16Cols + wave * 64 * NU;
+  if (nw >= sl.d) return;  // uniform: no barrier follows
+  const int rl = lane & 15;  // y row of the item this lane updates
+  const int g = lane >> 4;   // its rank group (operands) and column group (result)
+  const bool rowok = rl < it.nrows;
+  const int row = ix->rows[rowok ? rl : 0];
+  uint16_t *yrow = reinterpret_cast<uint16_t *>(a.y) + sl.col0 + (int64_t)row * a.ldy;
+  // y first (it depends on nothing else): the lane's 16 columns of each unit
+  uint4 yv[NU][2];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int64_t nc = nw + u * 64 + 16 * g;
+    const uint16_t *yp = yrow + (nc < sl.d ? nc : nw);
+    yv[u][0] = *reinterpret_cast<const uint4 *>(yp);
+    yv[u][1] = *reinterpret_cast<const uint4 *>(yp + 8);
+  }
+  const int kp = (r + 31) & ~31;  // ranks padded to the MFMA k step
+
+  // A operand: B_s rows of the permuted columns, ranks ks*32 + 8g .. + 7
+  const AdapterRef &ar = sl.ar;
+  const int cm = (rl >> 2) * 16 + (rl & 3);
+  bf16x8_t fa[RMX / 32][NU][4];
+#pragma unroll
+  for (int ks = 0; ks < RMX / 32; ++ks) {
+    if (ks > 0 && ks * 32 >= kp) break;  // uniform
+    const int j = ks * 32 + 8 * g;
+    const bool jok = j < r;
+    const int ja = jok ? j : 0;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int64_t n = nw + u * 64 + cm + 4 * cb;
+        const bool nok = n < sl.d;
+        const int64_t na = nok ? n : nw;
+        bf16x8_t v;
+        if constexpr (POOL) {
+          if ((r & 7) == 0) {
+            // r % 8 == 0: the 16-byte vector never straddles a page
+            const int64_t off = ((int64_t)r * ar.k + na * r + ja) * 2;
+            const int64_t page =
+                ar.page_table[(int64_t)it.adapter * ar.max_pages + (off >> ar.page_shift)];
+            v = ld16(ar.pool + (page << ar.page_shift) + (off & (ar.page_bytes - 1)));
+          } else {
+            uint16_t e8[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+              e8[w] = (jok && nok && j + w < r)
+                          ? *reinterpret_cast<const uint16_t *>(adapter_b_ptr(ar, it.adapter, r, na, j + w))
+                          : (uint16_t)0;
+            v = __builtin_bit_cast(bf16x8_t, e8);
+          }
+        } else {
+          v = ld16(ar.B + (((int64_t)it.adapter * ar.d + na) * ar.max_rank + ja) * 2);
+        }
+        fa[ks][u][cb] = keep_first(v, (jok && nok) ? r - j : 0);
+      }
+  }
+
+  // B operand: t[row][ks*32 + 8g .. + 7] as bf16 hi + lo (zero past the
+  // rank and for rows past the item)
+  const bool t_by_row = a.fused_cap > 0;
+  const float *tpart = reinterpret_cast<const float *>(a.ws + a.L.tpart);
+  bf16x8_t th[RMX / 32], tl[RMX / 32];
+#pragma unroll
+  for (int ks = 0; ks < RMX / 32; ++ks) {
+    if (ks > 0 && ks * 32 >= kp) break;  // uniform
+    const int j = ks * 32 + 8 * g;
+    const int ja = j < r ? j : 0;
+    float4 v0, v1;
+    if (t_by_row) {
+      const float *tp = tpart + ((int64_t)row * a.n_slices + slice) * a.L.R + ja;
+      v0 = *reinterpret_cast<const float4 *>(tp);
+      v1 = *reinterpret_cast<const float4 *>(tp + 4);
+    } else {
+      // the k-split partials, summed in split order (a rolled loop: the
+      // splits of 8 ranks are two float4 loads each)
+      const int64_t p = it.pos + (rowok ? rl : 0);
+      const float *tp = tpart + tpart_index(0, p, slice, ja, a.L.rows, a.n_slices, a.L.R);
+      const int64_t split_stride = (int64_t)a.L.rows * a.n_slices * a.L.R;
+      v0 = *reinterpret_cast<const float4 *>(tp);
+      v1 = *reinterpret_cast<const float4 *>(tp + 4);
+#pragma unroll 2
+      for (int qq = 1; qq < a.ksplit; ++qq) {
+        const float4 u0 = *reinterpret_cast<const float4 *>(tp + qq * split_stride);
+        const float4 u1 = *reinterpret_cast<const float4 *>(tp + qq * split_stride + 4);
+        v0.x += u0.x; v0.y += u0.y; v0.z += u0.z; v0.w += u0.w;
+        v1.x += u1.x; v1.y += u1.y; v1.z += u1.z; v1.w += u1.w;
+      }
+    }
+    const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const float x = (rowok && j + w < r) ? f[w] : 0.f;
+      h[w] = f32_to_bf16_bits(x);
+      l[w] = f32_to_bf16_bits(x - bf16_bits_to_f32(h[w]));
+    }
+    th[ks] = __builtin_bit_cast(bf16x8_t, h);
+    tl[ks] = __builtin_bit_cast(bf16x8_t, l);
+  }
+
+  const float scale = sl.scales[it.adapter];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    f32x4_t acc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < RMX / 32; ++ks) {
+      if (ks > 0 && ks * 32 >= kp) break;  // uniform
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][u][cb], th[ks], acc[cb], 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][u][cb], tl[ks], acc[cb], 0, 0, 0);
+      }
+    }
+    // y += scale * D' (lane: columns nc + 4 cb + i = acc[cb][i]), rounded once
+    const int64_t nc = nw + u * 64 + 16 * g;
+    if (!(rowok && nc < sl.d)) continue;
+    const uint16_t *o0 = reinterpret_cast<const uint16_t *>(&yv[u][0]);
+    const uint16_t *o1 = reinterpret_cast<const uint16_t *>(&yv[u][1]);
+    uint16_t e[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const uint16_t old = c < 8 ? o0[c] : o1[c - 8];
+      e[c] = f32_to_bf16_bits(bf16_bits_to_f32(old) + scale * acc[c >> 2][c & 3]);
+    }
+    uint4 w0, w1;
+    __builtin_memcpy(&w0, e, 16);
+    __builtin_memcpy(&w1, e + 8, 16);
+    *reinterpret_cast<uint4 *>(yrow + nc) = w0;
+    *reinterpret_cast<uint4 *>(yrow + nc + 8) = w1;
+  }
+}
+
 // 16-row items (decode batches).  (Capping its registers so that 4-6
 // workgroups fit per CU instead of 3 measured no faster at 4 and twice as
 // slow at 5-6, where it spills.)
@@ -696,7 +878,30 @@ hipError_t launch_expand_sgmv(const LoraArgs &a0, int rows_per_item, hipStream_t
   const int mode = !yfast ? 0 : slots8 ? 1 : pooled ? 2 : 0;
   bool r32 = true;
   for (int q = 0; q < a.n_slices; ++q) r32 = r32 && a.sl[q].ar.max_rank <= 32;
-  if (rows_per_item == 16)
+  // decode items on independent waves where the y runs, partial rows and B
+  // rows allow 16-byte accesses, and t is one split (folded into the base
+  // GEMM) or a sum of few: its rolled split sum is slower than expand_body's
+  // batched one past that (measured: 16 splits at the decode-4096 shape
+  // 5.9 -> 7.7 us, 7 at the 70B q+v shape 16.3 -> 22.8 us; folded t at that
+  // shape 16.2 -> 14.3 us, 4 splits at the paged-pool shape 28.7 -> 27.4 us)
+  bool w16 = rows_per_item == 16 && yfast && (slots8 || pooled) && (a.L.R % 8) == 0 &&
+             (a.fused_cap > 0 || a.ksplit <= 4);
+  for (int q = 0; q < a.n_slices; ++q) w16 = w16 && a.sl[q].d % 16 == 0;
+  if (w16) {
+    // kW16Cols-column blocks instead of ecb
+    a.col_blk[0] = 0;
+    for (int q = 0; q < a.n_slices; ++q)
+      a.col_blk[q + 1] = a.col_blk[q] + (int32_t)((a.sl[q].d + kW16Cols - 1) / kW16Cols);
+    const int64_t wb8 = ((int64_t)a.col_blk[a.n_slices] + 7) / 8 * 8;
+    const dim3 grid((unsigned)(a.L.items_g_cap * wb8));
+    if (pooled) {
+      if (r32) hipLaunchKernelGGL((k_expand_w16<32, true>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_expand_w16<RMAX_MFMA, true>), grid, dim3(256), 0, st, a);
+    } else {
+      if (r32) hipLaunchKernelGGL((k_expand_w16<32, false>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_expand_w16<RMAX_MFMA, false>), grid, dim3(256), 0, st, a);
+    }
+  } else if (rows_per_item == 16)
     expand_pick<16>(a, mode, r32, dim3((unsigned)(a.L.items_g_cap * cb8)), st);
   else
     expand_pick<64>(a, mode, r32, dim3((unsigned)(a.L.items_s_cap * cb8)), st);
