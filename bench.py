@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets")
     ap.add_argument("--path", default="auto", choices=["auto", "gather", "sgmv"])
+    ap.add_argument("--storage", default="slots", choices=["slots", "pool"],
+                    help="adapter storage of the timed step: rank-padded slots, or a paged pool "
+                         "of 2 MiB pages (unpadded A and B)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,14 +137,28 @@ def main():
         A, B = wl.slots(w, p)
         return A.to(dev), B.to(dev)
 
+    def pool_adapters(p, i):
+        pool, table, _n = wl.pool(w, p, page_bytes=2 << 20, seed_offset=i)
+        return pool.to(dev), table.to(dev)
+
     base = {"x": w.x.to(dev), "W": torch.cat([pq.W, pv.W], dim=0).contiguous().to(dev)}
-    base["Aq"], base["Bq"] = slot_adapters(pq)
-    base["Av"], base["Bv"] = slot_adapters(pv)
+    if args.storage == "slots":
+        base["Aq"], base["Bq"] = slot_adapters(pq)
+        base["Av"], base["Bv"] = slot_adapters(pv)
+    else:
+        base["Pq"], base["Tq"] = pool_adapters(pq, 0)
+        base["Pv"], base["Tv"] = pool_adapters(pv, 1)
     sets = []
     for i in range(args.sets):
         s = {kk: (v if i == 0 else v.clone()) for kk, v in base.items()}
-        s["slices"] = [lr.Slice(pq.d, lr.Adapters.slots(s["Aq"], s["Bq"], ranks), scales),
-                       lr.Slice(pv.d, lr.Adapters.slots(s["Av"], s["Bv"], ranks), scales)]
+        if args.storage == "slots":
+            s["slices"] = [lr.Slice(pq.d, lr.Adapters.slots(s["Aq"], s["Bq"], ranks), scales),
+                           lr.Slice(pv.d, lr.Adapters.slots(s["Av"], s["Bv"], ranks), scales)]
+        else:
+            s["slices"] = [lr.Slice(pq.d, lr.Adapters.paged(s["Pq"], s["Tq"], ranks, 2 << 20,
+                                                            w.max_rank), scales),
+                           lr.Slice(pv.d, lr.Adapters.paged(s["Pv"], s["Tv"], ranks, 2 << 20,
+                                                            w.max_rank), scales)]
         s["y"] = torch.empty(M, pq.d + pv.d, dtype=torch.bfloat16, device=dev)
         sets.append(s)
     set_bytes = sum(v.numel() * v.element_size() for kk, v in sets[0].items() if torch.is_tensor(v))
@@ -254,7 +271,7 @@ def main():
             "workload": "c3_proj70b_bf16: q 8192->8192 and v 8192->1024 LoRA linear, 512 decode "
                         "rows, 12 adapters ranks 4x3/16x6/64x3 alpha=2r, Zipf(1.1), 10% none",
             "M": M, "k": k, "d_q": pq.d, "d_v": pv.d, "n_adapters": w.S, "max_rank": w.max_rank,
-            "adapter_storage": "slots", "path": args.path, "buffer_sets": args.sets,
+            "adapter_storage": args.storage, "path": args.path, "buffer_sets": args.sets,
             "call": "lora_linear_sliced (q and v slices, W stacked [9216, 8192])",
             "buffer_set_mb": round(set_bytes / 1e6, 1),
         },

@@ -222,6 +222,20 @@ __device__ __forceinline__ void load16_to_lds_at(const uint8_t *src, void *lds) 
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
 
+// Start of row j of adapter a's A in slice q for the folded shrink (v =
+// slice << 16 | adapter << 8 | rank), or nullptr when a pool entry cannot
+// be used (outside the pool, or a page past the table).
+__device__ __forceinline__ const uint8_t *fused_arow(const FusedT &ft, int v, int K) {
+  const int q = v >> 16, a = (v >> 8) & 255, j = v & 255;
+  if (ft.page_table[q] == nullptr) return ft.A[q] + (((int64_t)a * ft.R[q] + j) * K) * 2;
+  const int64_t off = (int64_t)j * K * 2;
+  const int64_t idx = off >> ft.page_shift[q];
+  if (idx >= ft.max_pages[q]) return nullptr;
+  const int64_t page = ft.page_table[q][(int64_t)a * ft.max_pages[q] + idx];
+  if (page < 0 || page >= ft.n_pages[q]) return nullptr;
+  return ft.A[q] + (page << ft.page_shift[q]) + (off & ((int64_t(1) << ft.page_shift[q]) - 1));
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, bool PC, bool TX, int SK>
 __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
   constexpr int NC = WM * WN;                            // MFMA (consumer) waves
@@ -352,12 +366,8 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
         const int row = P >> 3;
         const int c = (P & 7) ^ (row & 7);
         const int v = row >= BN ? tmap[row - BN] : -1;
-        if (v >= 0) {
-          const int q = v >> 16, a = (v >> 8) & 255, j = v & 255;
-          tsrc[i] = ft.A[q] + (((int64_t)a * ft.R[q] + j) * p.K) * 2 + c * 16 + kbase;
-        } else {
-          tsrc[i] = reinterpret_cast<const uint8_t *>(xa) + c * 16 + kbase;
-        }
+        const uint8_t *arow = v >= 0 ? fused_arow(ft, v, p.K) : nullptr;
+        tsrc[i] = (arow ? arow : reinterpret_cast<const uint8_t *>(xa)) + c * 16 + kbase;
       }
     }
   };
@@ -605,13 +615,9 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
         // loads at clamped rows / a valid dummy row, all issued before use
         const int v1 = tmap[16 + (lane & 15)];
         const int kl = (lane >> 4) * 8;
-        const uint16_t *asrc;
-        if (v1 >= 0) {
-          const int q = v1 >> 16, a = (v1 >> 8) & 255, j = v1 & 255;
-          asrc = reinterpret_cast<const uint16_t *>(ft.A[q]) + ((int64_t)a * ft.R[q] + j) * p.K + kl;
-        } else {
-          asrc = p.x + (int64_t)m0 * p.ldx + kl;
-        }
+        const uint8_t *arow = v1 >= 0 ? fused_arow(ft, v1, p.K) : nullptr;
+        const uint16_t *asrc = arow ? reinterpret_cast<const uint16_t *>(arow) + kl
+                                    : p.x + (int64_t)m0 * p.ldx + kl;
         const uint16_t *xr[FM];
 #pragma unroll
         for (int i = 0; i < FM; ++i)

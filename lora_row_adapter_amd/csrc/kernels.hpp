@@ -107,8 +107,17 @@ hipError_t launch_translate(const AdapterRef &ar, int32_t S, int64_t n_pages,
 struct FusedT {
   int32_t cap;     // 16 x column tiles of the launch; 0: not fused
   int32_t n_slices, S;
-  const uint8_t *A[kMaxSlices];   // slot A [S][R][k] of each slice
-  int32_t R[kMaxSlices];          // max_rank of each slice (rank stride of A)
+  const uint8_t *A[kMaxSlices];   // slot A [S][R][k] of each slice, or its pool
+  int32_t R[kMaxSlices];          // max_rank of each slice (rank stride of slot A)
+  // pool slices (page_table != nullptr): A_s row j starts at logical byte
+  // j * 2k of adapter s, inside one page (the page size is a multiple of
+  // 2k); an entry outside [0, n_pages) or a page past max_pages makes the
+  // row read x instead (the plan counts such rows as bad pages, so their t
+  // is never used)
+  const int32_t *page_table[kMaxSlices];
+  int32_t max_pages[kMaxSlices];
+  int32_t page_shift[kMaxSlices];
+  int64_t n_pages[kMaxSlices];
   const int32_t *ranks[kMaxSlices];
   const int32_t *ids;             // adapter id of each row
   float *tpart;                   // partials region of the workspace

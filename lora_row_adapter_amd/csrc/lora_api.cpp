@@ -573,14 +573,18 @@ lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const
     int32_t fcap = 0;
     if (!qw && dtype == LORA_DTYPE_BF16 && use_mfma && !(flags & LORA_FLAG_SEPARATE_SHRINK) &&
         (int64_t)n_slices * S <= kFusedMaxEntries && S <= 256) {
-      bool slots = true;
+      // slots, or pools whose pages hold whole A rows (each row one
+      // contiguous run the GEMM's loads can take)
+      bool rows_ok = true;
       int64_t worst = 0;
       for (int q = 0; q < n_slices; ++q) {
-        slots = slots && slices[q].adapters.kind == LORA_ADAPTERS_SLOTS &&
-                ((uintptr_t)slices[q].adapters.A & 15u) == 0;
-        worst += (int64_t)S * slices[q].adapters.max_rank;
+        const lora_adapters_t &ad = slices[q].adapters;
+        rows_ok = rows_ok && (ad.kind == LORA_ADAPTERS_SLOTS
+                                  ? ((uintptr_t)ad.A & 15u) == 0
+                                  : ad.page_bytes % (2 * k) == 0);
+        worst += (int64_t)S * ad.max_rank;
       }
-      const int32_t cap = slots ? gemm_fused_cap(Mc, k, d_total, ldx, ldw) : 0;
+      const int32_t cap = rows_ok ? gemm_fused_cap(Mc, k, d_total, ldx, ldw) : 0;
       if (cap > 0 && worst <= 2 * (int64_t)cap) fcap = cap;
     }
     a.fused_cap = fcap;
@@ -590,9 +594,17 @@ lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const
       ft.n_slices = n_slices;
       ft.S = S;
       for (int q = 0; q < n_slices; ++q) {
-        ft.A[q] = (const uint8_t *)slices[q].adapters.A;
-        ft.R[q] = slices[q].adapters.max_rank;
-        ft.ranks[q] = slices[q].adapters.ranks;
+        const lora_adapters_t &ad = slices[q].adapters;
+        const bool pooled = ad.kind == LORA_ADAPTERS_POOL;
+        ft.A[q] = (const uint8_t *)(pooled ? ad.pool : ad.A);
+        ft.R[q] = ad.max_rank;
+        ft.ranks[q] = ad.ranks;
+        ft.page_table[q] = pooled ? ad.page_table : nullptr;
+        ft.max_pages[q] = pooled ? ad.max_pages : 0;
+        int sh = 0;
+        while (pooled && (int64_t(1) << sh) < ad.page_bytes) ++sh;
+        ft.page_shift[q] = sh;
+        ft.n_pages[q] = pooled ? ad.n_pages : 0;
       }
       ft.ids = adapter_ids + c0;
       ft.tpart = (float *)(ws + L.tpart);

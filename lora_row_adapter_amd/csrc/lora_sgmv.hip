@@ -712,6 +712,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void k
             const int64_t page =
                 ar.page_table[(int64_t)it.adapter * ar.max_pages + (off >> ar.page_shift)];
             v = ld16(ar.pool + (page << ar.page_shift) + (off & (ar.page_bytes - 1)));
+          } else if ((r & 3) == 0) {
+            // r % 4 == 0: two 8-byte halves, each 8-byte aligned (so inside
+            // one page); a half past the rank reads the first one again
+            uint2 hv[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int jh = (jok && j + 4 * hh < r) ? j + 4 * hh : ja;
+              const int64_t off = ((int64_t)r * ar.k + na * r + jh) * 2;
+              const int64_t page =
+                  ar.page_table[(int64_t)it.adapter * ar.max_pages + (off >> ar.page_shift)];
+              hv[hh] = *reinterpret_cast<const uint2 *>(ar.pool + (page << ar.page_shift) +
+                                                        (off & (ar.page_bytes - 1)));
+            }
+            v = __builtin_bit_cast(bf16x8_t, make_uint4(hv[0].x, hv[0].y, hv[1].x, hv[1].y));
           } else {
             uint16_t e8[8];
 #pragma unroll

@@ -159,3 +159,69 @@ def test_reuse_plan_with_fold():
     y1 = dw.run()
     y2 = dw.run(flags=lr.FLAG_REUSE_PLAN)
     assert torch.equal(y1, y2)
+
+
+def pooled_pair(w, page_bytes):
+    """Device slices for a two-projection workload with each slice's
+    adapters in its own paged pool (seeded physical pages, NaN elsewhere)."""
+    dev = torch.device("cuda")
+    ranks = torch.from_numpy(w.ranks).to(dev)
+    scales = torch.from_numpy(w.scales).to(dev)
+    slices, keep = [], []
+    for i, p in enumerate((w.proj("q"), w.proj("v"))):
+        pool, table, _n = wl.pool(w, p, page_bytes=page_bytes, seed_offset=i)
+        pool, table = pool.to(dev), table.to(dev)
+        keep.append((pool, table))
+        slices.append(lr.Slice(p.d, lr.Adapters.paged(pool, table, ranks, page_bytes, w.max_rank),
+                               scales))
+    W = torch.cat([w.proj("q").W, w.proj("v").W], dim=0).contiguous().to(dev)
+    return W, slices, keep
+
+
+@pytest.mark.parametrize("page_bytes", [4096, 1 << 20])
+def test_two_slices_fused_from_pools(oracle_mod, page_bytes):
+    """The fold reading A rows from paged pools ("S-LoRA: ...", "Unified
+    paging"): pages a multiple of the 1 KiB A row (k = 512), so every row
+    lies in one page; at 4 KiB an adapter's A spans up to 16 pages.  No
+    shrink launched; every row against the oracle; bitwise equal to the
+    same adapters in slots (same arithmetic, other addresses)."""
+    w = wl.c3_proj70b_bf16(M=400, k=512, d_q=8064, d_v=1152)
+    W, slices, _keep = pooled_pair(w, page_bytes)
+    x, ids = w.x.cuda(), torch.from_numpy(w.ids).cuda()
+    say("two pooled slices, fused shrink, %d-byte pages" % page_bytes)
+    res = {}
+    cnt = launches(lambda: res.setdefault("y", lr.lora_linear_sliced(x, W, slices, ids)))
+    y = res["y"]
+    assert cnt["gemm"] == 1 and cnt["sgmv_shrink"] == 0 and cnt["sgmv_expand"] == 1, cnt
+    for p, lo in ((w.proj("q"), 0), (w.proj("v"), 8064)):
+        ref = oracle_rows(oracle_mod, w, p)
+        err = normwise(y[:, lo:lo + p.d].double().cpu().numpy(), ref)
+        say("  %s normwise %.3g" % (p.name, err))
+        assert err <= 2e-2
+    Ws, sslices, _k2 = sliced_pair(w)
+    ys = lr.lora_linear_sliced(x, Ws, sslices, ids)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ys)
+
+
+def test_fused_pool_bad_page_entry_reads_no_adapter():
+    """A page-table entry outside the pool: the fold must not read through
+    it (its rows read x, their t is unused), the plan counts the adapter's
+    rows as bad pages and they get the base output."""
+    w = wl.c3_proj70b_bf16(M=400, k=512, d_q=8064, d_v=1152)
+    W, slices, keep = pooled_pair(w, 4096)
+    x, ids = w.x.cuda(), torch.from_numpy(w.ids).cuda()
+    table_q = keep[0][1]
+    bad = 9  # a rank-64 adapter: its A rows sit in the fold's columns
+    table_q[bad, 3] = 1 << 30
+    say("fused pool, page entry outside the pool")
+    ws = torch.zeros(lr.workspace_bytes_sliced(w.M, w.k, torch.bfloat16, slices),
+                     dtype=torch.uint8, device="cuda")
+    y = lr.lora_linear_sliced(x, W, slices, ids, workspace=ws)
+    chk = lr.lora_check(ws)
+    n_bad = int((w.ids == bad).sum())
+    assert n_bad > 0 and chk["n_bad_pages"] == n_bad, chk
+    base = lr.lora_gemm(x, W)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(np.flatnonzero(w.ids == bad)).cuda()
+    assert torch.equal(y[rows], base[rows])

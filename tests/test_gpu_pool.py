@@ -244,14 +244,17 @@ def test_managed_pools_c3_sliced_match_slots(c3_workload):
     W = torch.cat([dq.W, dv.W], 0).contiguous()
     managed = [lr.Slice(pq.d, qpool.adapters(), dq.scales), lr.Slice(pv.d, vpool.adapters(), dv.scales)]
     stacked = [lr.Slice(pq.d, dq.ad, dq.scales), lr.Slice(pv.d, dv.ad, dv.scales)]
+    # 64 KiB pages hold whole 16 KiB A rows, so both calls fold the shrink
+    # into the base GEMM: same arithmetic, other addresses
     y_m = lr.lora_linear_sliced(dq.x, W, managed, dq.ids)
-    # the same kernels on the slots (the slot call would otherwise fold the
-    # shrink into the base GEMM, which sums t in another order)
-    y_s = lr.lora_linear_sliced(dq.x, W, stacked, dq.ids, flags=lr.FLAG_SEPARATE_SHRINK)
     y_f = lr.lora_linear_sliced(dq.x, W, stacked, dq.ids)
+    # and both with the shrink as its own kernel
+    y_ms = lr.lora_linear_sliced(dq.x, W, managed, dq.ids, flags=lr.FLAG_SEPARATE_SHRINK)
+    y_s = lr.lora_linear_sliced(dq.x, W, stacked, dq.ids, flags=lr.FLAG_SEPARATE_SHRINK)
     torch.cuda.synchronize()
-    assert torch.equal(y_m, y_s)
-    assert normwise(y_f.double().cpu().numpy(), y_m.double().cpu().numpy()) <= 1e-2
+    assert torch.equal(y_m, y_f)
+    assert torch.equal(y_ms, y_s)
+    assert normwise(y_s.double().cpu().numpy(), y_m.double().cpu().numpy()) <= 1e-2
 
 
 @pytest.fixture(scope="module")
