@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--storage", default="slots", choices=["slots", "pool"],
                     help="adapter storage of the timed step: rank-padded slots, or a paged pool "
                          "of 2 MiB pages (unpadded A and B)")
+    ap.add_argument("--settle-ms", type=float, default=1500.0,
+                    help="untimed steps run for this long before the warmup, so the shader clock "
+                         "has settled whatever --warmup is (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -162,7 +165,7 @@ def main():
         s["y"] = torch.empty(M, pq.d + pv.d, dtype=torch.bfloat16, device=dev)
         sets.append(s)
     set_bytes = sum(v.numel() * v.element_size() for kk, v in sets[0].items() if torch.is_tensor(v))
-    ws = torch.empty(lr.workspace_bytes_sliced(M, k, torch.bfloat16, sets[0]["slices"]),
+    ws = torch.zeros(lr.workspace_bytes_sliced(M, k, torch.bfloat16, sets[0]["slices"]),
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log("%d buffer sets of %.0f MB" % (args.sets, set_bytes / 1e6))
@@ -185,6 +188,16 @@ def main():
             torch.cuda.synchronize()
             return prof, time.perf_counter() - t1
 
+    # settle: untimed steps until the clock holds steady (measured: with 20
+    # warmup steps and no settling the figure reads ~4% low)
+    settle_steps = 0
+    if args.settle_ms > 0:
+        t_s = time.perf_counter()
+        while (time.perf_counter() - t_s) * 1e3 < args.settle_ms:
+            for i in range(50):
+                step(settle_steps + i)
+            settle_steps += 50
+            torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -197,6 +210,8 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     value = M * args.steps / elapsed
+    y_timed = sets[(args.steps - 1) % len(sets)]["y"].clone()  # the last timed step's output
+    device_errors = lr.lora_check(ws, stream=stream)
     log("timed: %.3f ms/step, %.3g tokens/s" % (ms_per_step, value))
 
     # the same steps again with per-launch events (library-side, on the
@@ -208,6 +223,32 @@ def main():
            for kname in lr.KERNEL_CLASSES}
     launches = {kname: prof[kname]["launches"] for kname in lr.KERNEL_CLASSES}
     log("per-launch us: " + json.dumps({k_: round(v, 2) for k_, v in per.items()}))
+
+    # per-step GPU time from events between steps on the stream (rotating
+    # buffer sets, as timed), and the same with one buffer set only (warm:
+    # x, W and the adapters stay in the Infinity Cache, as for a layer whose
+    # input was just written)
+    def step_times(n, same_set):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record(stream)
+        for i in range(n):
+            step(0 if same_set else i)
+            evs[i + 1].record(stream)
+        evs[-1].synchronize()
+        return np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n)])
+    cold = step_times(prof_steps, False)
+    warm = step_times(prof_steps, True)
+
+    def dist(a):
+        return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+                "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+    step_us = {"rotating_sets": dist(cold), "warm_same_buffer": dist(warm),
+               "tokens_per_s_at_median": round(M / (np.median(cold) * 1e-6), 1),
+               "warm_tokens_per_s_at_median": round(M / (np.median(warm) * 1e-6), 1),
+               "what": "GPU time per step between events on the launch stream; rotating_sets = the "
+                       "timed configuration, warm_same_buffer = one buffer set reused (inputs resident "
+                       "in the Infinity Cache)"}
+    log("step us: " + json.dumps(step_us))
 
     bq = wl.algorithmic_bytes(w, pq)
     bv = wl.algorithmic_bytes(w, pv)
@@ -304,7 +345,12 @@ def main():
             "expand_frac_hbm": round(expand_gbs / HBM_PEAK_GBS, 4),
             "algorithmic": {"q": bq, "v": bv, "fused_shrink_bytes": shrink_bytes},
         },
+        "step_us": step_us,
+        "device_errors": device_errors,
+        "settle": {"steps": settle_steps, "ms": args.settle_ms},
     }
+    if not args.no_others:
+        result["gather_path"] = gather_path(lr, wl, w, sets, ids, ws, stream, step)
 
     if not args.no_activation:
         result["adapter_activation"] = adapter_activation(lr, w, pq, pv, stream)
@@ -315,7 +361,10 @@ def main():
     if not args.no_others:
         result["other_configs"] = other_configs(lr, wl, stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, pq, pv, args.cpu_seconds)
+        y_last = y_timed.double().cpu().numpy()
+        result["cpu_baseline"], result["output_check"] = cpu_baseline(w, pq, pv, args.cpu_seconds,
+                                                                      y_last)
+        result["oracle_seconds"] = oracle_seconds(wl, w)
     print(json.dumps(result), flush=True)
 
 
@@ -536,21 +585,33 @@ def adapter_activation(lr, w, pq, pv, stream, page_bytes=65536, reps=20):
     return res
 
 
-def cpu_baseline(w, pq, pv, target_s):
-    """The fp64 oracle, as it is, on a bounded sample of the same rows."""
+def cpu_baseline(w, pq, pv, target_s, y_gpu):
+    """The fp64 oracle, as it is, on a bounded sample of the same rows; the
+    first full pass also checks the last timed step's output (y_gpu, both
+    projections, every row) at the layer's bf16 bound."""
     import oracle
     threads = oracle.default_threads()
     used = oracle.threads_used(threads)
     rng = np.random.default_rng(0)
     order = rng.permutation(w.M)
+    check = {}
 
     def run(rows):
         t0 = time.perf_counter()
+        outs = []
         for p in (pq, pv):
-            oracle.lora_linear(w.x[torch.from_numpy(rows)], p.W, p.A, p.B,
-                               w.scales.astype(np.float64), w.ids[rows], max_rank=w.max_rank,
-                               n_threads=threads)
-        return time.perf_counter() - t0
+            outs.append(oracle.lora_linear(w.x[torch.from_numpy(rows)], p.W, p.A, p.B,
+                                           w.scales.astype(np.float64), w.ids[rows],
+                                           max_rank=w.max_rank, n_threads=threads))
+        el = time.perf_counter() - t0
+        if len(rows) == w.M and not check:
+            for name, ref, lo, hi in (("q", outs[0], 0, pq.d), ("v", outs[1], pq.d, pq.d + pv.d)):
+                got = y_gpu[np.asarray(rows)][:, lo:hi]
+                check["normwise_" + name] = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+            check["tol"] = 2e-2
+            check["rows"] = int(len(rows))
+            check["ok"] = all(check["normwise_" + n] <= 2e-2 for n in ("q", "v"))
+        return el
 
     probe = np.sort(order[:used])
     t_probe = run(probe)
@@ -563,9 +624,90 @@ def cpu_baseline(w, pq, pv, target_s):
         t += run(rows)
         passes += 1
     log("cpu oracle: %d rows x %d passes in %.1f s on %d threads" % (n, passes, t, used))
-    return {"value": n * passes / t, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": "%d of the 512 rows (seeded) x %d passes, q and v projections, fp64, %.1f s"
-                      % (n, passes, t)}
+    if not check:  # the sample stopped short of every row: check those it covered
+        check = {"rows": 0, "ok": None, "note": "the oracle sample did not cover a full pass"}
+    log("output check: " + json.dumps(check))
+    return ({"value": n * passes / t, "unit": "tokens/s", "cores": used, "kind": "oracle",
+             "sample": "%d of the 512 rows (seeded) x %d passes, q and v projections, fp64, %.1f s"
+                       % (n, passes, t)}, check)
+
+
+def oracle_seconds(wl, w3):
+    """One full oracle pass of every workload on all host threads, and of
+    the two small ones on one thread (fp64, seconds per pass)."""
+    import oracle
+    threads = oracle.default_threads()
+    out = {"threads": oracle.threads_used(threads)}
+    for name, make in (("c0_tiny_fp32", wl.c0_tiny_fp32), ("c1_decode_bf16", wl.c1_decode_bf16),
+                       ("c2_prefill_bf16", wl.c2_prefill_bf16), ("c3_proj70b_bf16", None),
+                       ("c4_paged_bf16", wl.c4_paged_bf16)):
+        w = w3 if make is None else make()
+        entry = {}
+        for nt in ((threads, 1) if name in ("c0_tiny_fp32", "c1_decode_bf16") else (threads,)):
+            t0 = time.perf_counter()
+            for p in w.projections:
+                oracle.lora_linear(w.x, p.W, p.A, p.B, w.scales.astype(np.float64), w.ids,
+                                   max_rank=w.max_rank, n_threads=nt)
+            entry["s_%d_threads" % oracle.threads_used(nt)] = round(time.perf_counter() - t0, 4)
+        entry["rows"] = w.M
+        out[name] = entry
+        del w
+    log("oracle seconds: " + json.dumps(out))
+    return out
+
+
+def gather_path(lr, wl, w3, sets, ids, ws, stream, step_fn, steps=200):
+    """The VALU gather kernels (LDS-staged A tiles, wavefront reduction
+    over k) at the 70B q+v step and at the decode-4096 workload: step time
+    and their event-timed shrink / expand launches."""
+    out = {}
+    for name in ("c3_proj70b_bf16", "c1_decode_bf16"):
+        if name == "c3_proj70b_bf16":
+            def go(i):
+                s_ = sets[i % len(sets)]
+                lr.lora_linear_sliced(s_["x"], s_["W"], s_["slices"], ids, y=s_["y"], workspace=ws,
+                                      path=lr.PATH_GATHER, stream=stream)
+            M = w3.M
+            alg = [wl.algorithmic_bytes(w3, w3.proj("q")), wl.algorithmic_bytes(w3, w3.proj("v"))]
+        else:
+            w = wl.c1_decode_bf16()
+            p = w.projections[0]
+            dev = torch.device("cuda:0")
+            A, B = wl.slots(w, p)
+            ad = lr.Adapters.slots(A.to(dev), B.to(dev), torch.from_numpy(w.ranks).to(dev))
+            x, W = w.x.to(dev), p.W.to(dev)
+            y = torch.empty(w.M, p.d, dtype=w.dtype, device=dev)
+            ids1, sc = torch.from_numpy(w.ids).to(dev), torch.from_numpy(w.scales).to(dev)
+            ws1 = lr.new_workspace(w.M, p.d, w.k, w.dtype, ad, device=dev)
+
+            def go(i):
+                lr.lora_linear(x, W, ad, ids1, sc, y=y, workspace=ws1, path=lr.PATH_GATHER,
+                               stream=stream)
+            M = w.M
+            alg = [wl.algorithmic_bytes(w, p)]
+        for i in range(100):
+            go(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            go(i)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        with lr.Profiler():
+            for i in range(steps):
+                go(i)
+            prof = lr.Profiler.read(reset=True)
+            torch.cuda.synchronize()
+        per = {k: round(prof[k]["ms"] * 1e3 / prof[k]["launches"], 2) for k in lr.KERNEL_CLASSES
+               if prof[k]["launches"]}
+        shr_b = sum(a["shrink_bytes"] for a in alg) - (alg[0]["M_a"] * w3.k * 2 if len(alg) == 2 else 0)
+        exp_b = sum(a["expand_bytes"] for a in alg)
+        out[name] = {"tokens_per_s": round(M * steps / el, 1), "ms_per_step": round(el * 1e3 / steps, 4),
+                     "per_launch_us": per,
+                     "shrink_gbs": round(shr_b / per["shrink"] / 1e3, 1) if "shrink" in per else None,
+                     "expand_gbs": round(exp_b / per["expand"] / 1e3, 1) if "expand" in per else None}
+    log("gather path: " + json.dumps(out))
+    return out
 
 
 if __name__ == "__main__":
