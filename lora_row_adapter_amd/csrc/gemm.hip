@@ -20,6 +20,7 @@
 #include <atomic>
 
 #include "kernels.hpp"
+#include "plan_body.hpp"
 
 namespace lora {
 
@@ -177,6 +178,10 @@ struct PipeArgs {
   uint64_t epoch;
   int32_t spin_limit;
   int32_t *expired;
+  // split-K pairs: the plan of the layer's batch, run by the first-arriving
+  // workgroup of pair 0 once its partial is out (has_plan != 0)
+  int32_t has_plan;
+  PlanArgs plan;
 };
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -551,6 +556,12 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       }
       __syncthreads();
       if (tid == 0) __hip_atomic_store(ready, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // The layer's plan needs only the row ids: this workgroup, its half
+      // of the tile handed over, runs it in its freed LDS while the other
+      // half finishes the tile -- so the plan needs no kernel, stream or
+      // event of its own, and the kernels after the GEMM see it in stream
+      // order
+      if (p.has_plan && pair == 0) plan_detail::plan_body<NT>(p.plan, smem, sizeof(smem));
       return;
     }
     if (tid == 0) {
@@ -845,7 +856,10 @@ std::atomic<uint64_t> g_epoch{0x9E3779B97F4A7C15ull};
 constexpr int32_t kSpinDefault = 1 << 22;  // polls of ~2 x 64 clocks: ~0.3 s
 std::atomic<int32_t> g_spin_limit{kSpinDefault};
 template <bool TX>
-void launch_split(PipeArgs pa, int64_t M, int64_t d, void *gws, int32_t *expired, hipStream_t st) {
+void launch_split(PipeArgs pa, int64_t M, int64_t d, void *gws, int32_t *expired, hipStream_t st,
+                  const PlanArgs *plan) {
+  pa.has_plan = plan != nullptr;
+  if (plan) pa.plan = *plan;
   const int64_t P = split_pairs(M, d);
   pa.tiles_m = (int)((M + kSplitBM - 1) / kSplitBM);
   pa.tiles_n = (int)((d + kSplitBN - 1) / kSplitBN);
@@ -882,9 +896,15 @@ void set_sync_spin_limit(int32_t polls) {
   g_spin_limit.store(polls < 0 ? kSpinDefault : polls, std::memory_order_relaxed);
 }
 
+bool gemm_runs_plan(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
+                    void *gws, size_t gws_bytes) {
+  return dtype == 1 && M > 0 && d > 0 && pipe_ok(k, ldx, ldw) && choose_tile(M, d) == 2 &&
+         split_ok(M, k, d, gws, gws_bytes);
+}
+
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, void *gws,
-                       size_t gws_bytes, hipStream_t st, int32_t *expired) {
+                       size_t gws_bytes, hipStream_t st, int32_t *expired, const PlanArgs *plan) {
   if (M <= 0 || d <= 0) return hipSuccess;
   if (dtype == 1) {
     if (pipe_ok(k, ldx, ldw)) {
@@ -894,7 +914,7 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
         case 1: launch_pipe<256, 128, 4, 1, 3>(pa, st); break;
         case 2:
           if (split_ok(M, k, d, gws, gws_bytes)) {
-            launch_split<false>(pa, M, d, gws, expired, st);
+            launch_split<false>(pa, M, d, gws, expired, st, plan);
           } else {
             launch_pipe<128, 144, 4, 1, 3>(pa, st);
           }
@@ -972,14 +992,15 @@ bool gemm_footprint(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx,
 
 hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                              const void *W, int64_t ldw, void *y, int64_t ldy, const FusedT &ft,
-                             void *gws, size_t gws_bytes, hipStream_t st, int32_t *expired) {
+                             void *gws, size_t gws_bytes, hipStream_t st, int32_t *expired,
+                             const PlanArgs *plan) {
   if (ft.cap <= 0 || ft.cap != gemm_fused_cap(M, k, d, ldx, ldw) ||
       ft.n_slices * ft.S > kFusedMaxEntries || ft.S > 256 || ft.n_slices > kMaxSlices)
     return hipErrorInvalidValue;
   PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
   pa.ft = ft;
   if (split_ok(M, k, d, gws, gws_bytes)) {
-    launch_split<true>(pa, M, d, gws, expired, st);
+    launch_split<true>(pa, M, d, gws, expired, st, plan);
   } else {
     launch_pipe<128, 144, 4, 1, 3, true>(pa, st);
   }

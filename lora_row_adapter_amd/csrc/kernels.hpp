@@ -131,9 +131,16 @@ constexpr int kFusedMaxEntries = 256;  // n_slices * S the fused path scans
 // holds that many bytes, else the unsplit tiles (another summation order).
 // expired: where split-K pairs count expired waits (nullptr: word
 // kHdrSyncExpired of the GEMM region's own 256-byte header).
+// plan: run this plan inside the launch (only where gemm_runs_plan says
+// the launch can carry it; else nullptr).
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, void *gws,
-                       size_t gws_bytes, hipStream_t st, int32_t *expired = nullptr);
+                       size_t gws_bytes, hipStream_t st, int32_t *expired = nullptr,
+                       const PlanArgs *plan = nullptr);
+// Whether the base GEMM of this shape and GEMM region runs split-K pairs,
+// whose first-arriving workgroup of pair 0 can run the layer's plan.
+bool gemm_runs_plan(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
+                    void *gws, size_t gws_bytes);
 // Bound of the split-K pairs' wait in polls for later launches (< 0: the
 // default); a test hook that makes every wait expire at once with 0.
 void set_sync_spin_limit(int32_t polls);
@@ -146,7 +153,7 @@ int32_t gemm_fused_cap(int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw
 hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                              const void *W, int64_t ldw, void *y, int64_t ldy, const FusedT &ft,
                              void *gws, size_t gws_bytes, hipStream_t st,
-                             int32_t *expired = nullptr);
+                             int32_t *expired = nullptr, const PlanArgs *plan = nullptr);
 // Base GEMM with a quantized weight (bf16 x and y).
 struct QGemmArgs {
   int32_t fmt;  // 1 INT8 (per-row scales), 2 INT4 (per-row, per-k-group scales)

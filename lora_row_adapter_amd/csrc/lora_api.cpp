@@ -624,7 +624,14 @@ lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const
     hipStream_t ps = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     const bool reuse = (flags & LORA_FLAG_REUSE_PLAN) != 0;
-    bool beside = !self_contained;
+    // Where the base GEMM runs split-K pairs, its first-arriving workgroup
+    // of pair 0 runs the plan (no plan launch, side stream or events: the
+    // fork and join cost ~6.5 us each on the stream at the 70B q+v step)
+    const bool in_gemm = !reuse && !qw &&
+                         gemm_runs_plan(dtype, Mc, k, d_total, ldx, ldw, gws, gws_bytes);
+    PlanArgs gplan{};
+    if (in_gemm) gplan = make_plan_args(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L);
+    bool beside = !self_contained && !in_gemm;
     if (!reuse && !qw && beside) {
       KernelFootprint pf, gf;
       const PlanArgs pa = make_plan_args(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L);
@@ -633,7 +640,7 @@ lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const
                fits_beside(gf, pf);
     }
     const bool fork = !reuse && beside && !self_contained && side::get(&ps, &ev_fork, &ev_join);
-    if (!reuse) {
+    if (!reuse && !in_gemm) {
       if (fork) {
         if (hipEventRecord(ev_fork, st) != hipSuccess || hipStreamWaitEvent(ps, ev_fork, 0) != hipSuccess)
           return LORA_ERR_HIP;
@@ -648,11 +655,12 @@ lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const
       // expired split-K waits are counted in the plan header, where
       // lora_check reads them
       int32_t *expired = reinterpret_cast<int32_t *>(ws + L.hdr) + kHdrSyncExpired;
+      const PlanArgs *pp = in_gemm ? &gplan : nullptr;
       if (fcap > 0)
         return launch_gemm_fused(Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, ft, gws, gws_bytes, st,
-                                 expired);
+                                 expired, pp);
       return launch_gemm(dtype, Mc, k, d_total, xc, ldx, W, ldw, yc, ldy, gws, gws_bytes, st,
-                         expired);
+                         expired, pp);
     });
     if (e != hipSuccess) return LORA_ERR_HIP;
     if (fork && hipStreamWaitEvent(st, ev_join, 0) != hipSuccess) return LORA_ERR_HIP;

@@ -56,6 +56,39 @@ def counters_per_dispatch(pmc_dir: str) -> Dict[str, Dict[str, float]]:
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
 
 
+COMPUTE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                    "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_WAVE_CYCLES "
+                    "SQ_WAVES GRBM_GUI_ACTIVE")
+N_CU, N_SIMD = 256, 1024
+
+
+def compute_counters(pmc_dir: str) -> Dict[str, dict]:
+    """Per kernel: mean counters per dispatch and mean duration, from a
+    `--pmc <COMPUTE_COUNTERS> --kernel-trace` run, with derived figures:
+    MFMA busy fraction (MFMA-busy cycles per SIMD over CU-busy cycles per
+    CU), effective shader clock (CU-busy cycles per CU over the dispatch's
+    duration) and MFMA TFLOP/s (MOPS count units of 512 flops)."""
+    per = counters_per_dispatch(pmc_dir)
+    durs = defaultdict(list)
+    for f in glob.glob(os.path.join(pmc_dir, "*kernel_trace.csv")):
+        for r in csv.DictReader(open(f)):
+            durs[kernel_short_name(r["Kernel_Name"])].append(
+                (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3)
+    out = {}
+    for k, cs in per.items():
+        d = sum(durs[k]) / len(durs[k]) if durs.get(k) else None
+        e = {"counters": cs, "duration_us": d}
+        busy = cs.get("SQ_BUSY_CU_CYCLES", 0.0) / N_CU
+        mfma = cs.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / N_SIMD
+        if busy > 0:
+            e["mfma_busy_frac"] = mfma / busy
+        if d:
+            e["shader_clock_ghz"] = busy / (d * 1e3)
+            e["mfma_tflops"] = cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / (d * 1e-6) / 1e12
+        out[k] = e
+    return out
+
+
 def copy_factor(pmc_dir: str, counter: str, copy_bytes: int) -> float:
     """Counter reading (KiB) per byte actually moved, from the copy kernel."""
     cs = counters_per_dispatch(pmc_dir)
@@ -107,6 +140,28 @@ def summarize(root: str, out_dir: str, bench_cmd: str, copy_mib: int, gemm_sourc
         wb = wk * 1024.0 / w_fac
         traffic[k] = {"fetch_bytes": fb, "write_bytes": wb}
         lines.append("| %s | %.1f | %.1f | %.2f | %.2f |" % (k, fk, wk, fb / 1e6, wb / 1e6))
+    cdir = os.path.join(root, "compute")
+    compute = compute_counters(cdir) if os.path.isdir(cdir) else {}
+    if compute:
+        lines += ["", "## MFMA, clock and LDS counters per dispatch", "",
+                  "    rocprofv3 --kernel-trace --pmc %s --output-format csv -d <out>/compute "
+                  "-o compute -- %s" % (COMPUTE_COUNTERS, bench_cmd), "",
+                  "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / %d SIMDs over SQ_BUSY_CU_CYCLES / %d CUs; "
+                  "shader clock = SQ_BUSY_CU_CYCLES / %d CUs over the dispatch duration of the same "
+                  "run; MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops over the duration."
+                  % (N_SIMD, N_CU, N_CU), "",
+                  "| kernel | us (this run) | MFMA busy | shader clock GHz | MFMA TFLOP/s | "
+                  "LDS active cyc / CU | LDS bank-conflict cyc / CU | waves |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for k, e in sorted(compute.items(), key=lambda kv: -(kv[1]["duration_us"] or 0)):
+            c = e["counters"]
+            lines.append("| %s | %s | %s | %s | %s | %.0f | %.0f | %.0f |" % (
+                k, "%.2f" % e["duration_us"] if e["duration_us"] else "-",
+                "%.3f" % e["mfma_busy_frac"] if "mfma_busy_frac" in e else "-",
+                "%.2f" % e["shader_clock_ghz"] if "shader_clock_ghz" in e else "-",
+                "%.1f" % e["mfma_tflops"] if "mfma_tflops" in e else "-",
+                c.get("SQ_LDS_IDX_ACTIVE", 0) / N_CU, c.get("SQ_LDS_BANK_CONFLICT", 0) / N_CU,
+                c.get("SQ_WAVES", 0)))
     md = os.path.join(out_dir, "c3_proj70b_kernels.md")
     open(md, "w").write("\n".join(lines) + "\n")
     # the headline step's GEMM: the split-K pairs with the shrink folded in
@@ -115,7 +170,9 @@ def summarize(root: str, out_dir: str, bench_cmd: str, copy_mib: int, gemm_sourc
                    k.startswith("k_gemm_bf16_pipe")),
                   key=lambda k: (not k.startswith("k_gemm_bf16_split"), "true" not in k, k))
     result = {"workload": workload, "kernel_trace": stats, "traffic": traffic,
-              "fetch_factor": f_fac, "write_factor": w_fac}
+              "fetch_factor": f_fac, "write_factor": w_fac,
+              "compute": {k: {kk: vv for kk, vv in e.items() if kk != "counters"}
+                          for k, e in compute.items()}}
     if gemm:
         g = gemm[0]
         tj = {
