@@ -67,9 +67,14 @@ typedef enum lora_status {
   LORA_ERR_UNSUPPORTED = 8  /* valid request that this library does not implement */
 } lora_status_t;
 
+/* The two range enumerators of the enums a caller passes in make every
+ * int32 value a valid value of the type (a C caller may pass any int; the
+ * library checks it and answers LORA_ERR_DTYPE / LORA_ERR_ARG). */
 typedef enum lora_dtype {
   LORA_DTYPE_F32 = 0,   /* x, W, A, B, y in fp32; true fp32 products, fp32 accumulation */
-  LORA_DTYPE_BF16 = 1   /* x, W, A, B, y in bf16; fp32 accumulation, RNE on store */
+  LORA_DTYPE_BF16 = 1,  /* x, W, A, B, y in bf16; fp32 accumulation, RNE on store */
+  LORA_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  LORA_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } lora_dtype_t;
 
 typedef enum lora_path {
@@ -91,7 +96,9 @@ typedef enum lora_path {
 /* Where adapter weights live. */
 typedef enum lora_adapter_kind {
   LORA_ADAPTERS_SLOTS = 0,  /* stacked, rank-padded slots */
-  LORA_ADAPTERS_POOL = 1    /* unified pool of fixed-size pages + per-adapter page table */
+  LORA_ADAPTERS_POOL = 1,   /* unified pool of fixed-size pages + per-adapter page table */
+  LORA_ADAPTERS_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  LORA_ADAPTERS_RANGE_MAX_ = 0x7FFFFFFF
 } lora_adapter_kind_t;
 
 /*

@@ -63,5 +63,42 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def clang_asan_runtime() -> str:
+    """The ASan runtime of the ROCm clang that hipcc drives (preloaded by a
+    process that loads a sanitized build)."""
+    import glob
+    for c in sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")):
+        return c
+    raise RuntimeError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+
+
+def build_sanitized(out_dir: str) -> str:
+    """The library with its host code built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code as usual), as
+    out_dir/liblora_row.so.  The sanitizer runtime is not linked in: the
+    process that loads it preloads clang_asan_runtime()."""
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
+           "-g"]
+
+    def comp(src):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc()] + common_flags() + san + ["-x", "hip", "-c", os.path.join(CSRC, src),
+                                                  "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("sanitized hipcc failed for %s:\n%s" % (src, r.stdout + r.stderr))
+        return obj
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    lib = os.path.join(out_dir, "liblora_row.so")
+    cmd = [hipcc(), "--offload-arch=%s" % ARCH, "-shared", "-fPIC", "-o", lib] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stdout + r.stderr)
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)

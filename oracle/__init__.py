@@ -27,16 +27,21 @@ ROW_ADAPTED, ROW_NONE, ROW_BAD_ID, ROW_BAD_RANK, ROW_BAD_PAGE = 0, 1, 2, 3, 4
 _lib = None
 
 
-def build(force: bool = True, out: str | None = None, mutant: int = 0) -> str:
+def build(force: bool = True, out: str | None = None, mutant: int = 0,
+          sanitize: bool = False) -> str:
     """Compile the oracle with gcc (-O2 -fopenmp -ffp-contract=off).
 
-    ``mutant`` > 0 builds a copy with one planted mistake (pin tests only)."""
+    ``mutant`` > 0 builds a copy with one planted mistake (pin tests only);
+    ``sanitize`` builds it under AddressSanitizer and UndefinedBehaviorSanitizer
+    (the loading process preloads gcc's libasan)."""
     out = out or _LIB
     if force or not os.path.exists(out):
         tmp = out + ".tmp%d" % os.getpid()
+        san = (["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                "-fno-omit-frame-pointer", "-g"] if sanitize else [])
         cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-               "-std=c99", "-Wall", "-Werror", "-DORACLE_MUTANT=%d" % int(mutant), _SRC,
-               "-o", tmp]
+               "-std=c99", "-Wall", "-Werror", "-DORACLE_MUTANT=%d" % int(mutant)] + san + [
+               _SRC, "-o", tmp]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out
