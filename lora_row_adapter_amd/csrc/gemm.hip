@@ -18,6 +18,7 @@
 //
 // fp32: plain VALU FMA tiles (64 x 64, 4 x 4 per thread); true fp32 products.
 #include <atomic>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "plan_body.hpp"
@@ -486,12 +487,87 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       if (s < nk) issue(s, s);
   }
   if constexpr (!PC) {
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_tile(kt);
+    // One MFMA wave per SIMD that also issues its share of the tile loads
+    // (256 x 256 tiles: the accumulators take a SIMD's registers).  Nothing
+    // else hides the fragment reads, so they are double-buffered: k-step
+    // 1's fragments load during k-step 0's MFMAs, the next tile's k-step 0
+    // fragments during k-step 1's (its barrier comes between the two, once
+    // this tile's reads have landed).  The reads are explicit ds_read_b128
+    // with explicit lgkmcnt waits: as ordinary loads the compiler cannot tell
+    // them from the stages the DMA is still filling and waits for every load
+    // in flight before each read (then each read's latency was exposed:
+    // 43% MFMA busy at the 8192 x 4096 x 4096 prefill shape).
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    u32x4v fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+    auto lfrag = [&](int soff, int ks, u32x4v (&af)[FM], u32x4v (&bfr)[FN]) {
+      const int pc = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+      const uint32_t ao = lds0 + soff + (wm0 + (lane & 15)) * BKB + pc;
+      const uint32_t bo = lds0 + soff + A_BYTES + (wn0 + (lane & 15)) * BKB + pc;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(af[i]) : "v"(ao), "i"(i * 16 * BKB));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(bfr[j]) : "v"(bo), "i"(j * 16 * BKB));
+    };
+    // at most N LDS reads outstanding; the fragments pass through the
+    // statements, so nothing reads them before the wait
+    auto fwait = [&](auto nconst, u32x4v (&af)[FM], u32x4v (&bfr)[FN]) {
+      constexpr int N = decltype(nconst)::value;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(af[i]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(bfr[j]));
+      asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(af[i]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(bfr[j]));
+    };
+    // the waits count LDS reads in order: once at most FM + FN of the
+    // later set are outstanding (15 at most, the counter's range), the
+    // earlier set has landed
+    constexpr int NFR = FM + FN < 15 ? FM + FN : 15;
+    auto mma = [&](const u32x4v (&af)[FM], const u32x4v (&bfr)[FN]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
+                                                              __builtin_bit_cast(bf16x8_t, bfr[j]),
+                                                              acc[i][j], 0, 0, 0);
+    };
+    wait_tile(0);
+    barrier();
+    if (STAGES - 1 < nk) issue(STAGES - 1, (STAGES - 1) % STAGES);
+    lfrag(0, 0, fa0, fb0);
+    // the last tile is peeled off so that the loop body has no branch
+    // around the next tile's reads (the compiler would merge the wait counts
+    // of both paths and wait for those reads too)
+    for (int kt = 0; kt < nk - 1; ++kt) {
+      lfrag((kt % STAGES) * STAGE_BYTES, 1, fa1, fb1);
+      fwait(std::integral_constant<int, NFR>{}, fa0, fb0);
+      mma(fa0, fb0);
+      // the k-step-0 MFMAs stay ahead of the wait for the next tile's loads
+      // (the scheduler would otherwise sink them past the barrier and the
+      // wait would no longer overlap them)
+      __builtin_amdgcn_sched_barrier(0);
+      wait_tile(kt + 1);
+      // this wave's reads of tile kt are in registers before the barrier
+      // that lets tile kt + STAGES overwrite its stage
+      fwait(std::integral_constant<int, 0>{}, fa1, fb1);
       barrier();
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-      compute(kt);
+      if (kt + STAGES < nk) issue(kt + STAGES, (kt + STAGES) % STAGES);
+      lfrag(((kt + 1) % STAGES) * STAGE_BYTES, 0, fa0, fb0);
+      mma(fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    lfrag(((nk - 1) % STAGES) * STAGE_BYTES, 1, fa1, fb1);
+    fwait(std::integral_constant<int, NFR>{}, fa0, fb0);
+    mma(fa0, fb0);
+    fwait(std::integral_constant<int, 0>{}, fa1, fb1);
+    mma(fa1, fb1);
   } else if (producer) {
     for (int kt = 0; kt < nk; ++kt) {
       wait_tile(kt);
