@@ -378,7 +378,10 @@ def other_configs(lr, wl, stream, n_sets=4, steps=200, warmup=100):
       c4_paged_bf16    2048 rows from 256 sequences, d = k = 5120, 1024 adapters
                        of rank 16 in a paged pool, ~131 present
     Per workload: tokens/s, event-timed launches, the base GEMM's TFLOP/s and
-    the shrink / expand GB/s against the algorithmic bytes of the instance."""
+    the shrink / expand GB/s against the algorithmic bytes of the instance.
+    The base GEMM's launch carries the layer's plan; its TFLOP/s is taken
+    from a pass that reuses the plan already in the workspace (the launch
+    without it), and plan_in_gemm_us is what carrying the plan adds."""
     dev = torch.device("cuda:0")
     out = {}
     for name, make, storage in (("c1_decode_bf16", wl.c1_decode_bf16, "slots"),
@@ -402,9 +405,9 @@ def other_configs(lr, wl, stream, n_sets=4, steps=200, warmup=100):
         ys = [torch.empty(M, p.d, dtype=w.dtype, device=dev) for _ in range(n_sets)]
         ws = lr.new_workspace(M, p.d, w.k, w.dtype, ad, device=dev)
 
-        def step(i):
+        def step(i, flags=0):
             lr.lora_linear(xs[i % n_sets], Ws[i % n_sets], ad, ids, scales, y=ys[i % n_sets],
-                           workspace=ws, stream=stream)
+                           workspace=ws, flags=flags, stream=stream)
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
@@ -413,22 +416,30 @@ def other_configs(lr, wl, stream, n_sets=4, steps=200, warmup=100):
             step(i)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        with lr.Profiler():
-            for i in range(steps):
-                step(i)
-            prof = lr.Profiler.read(reset=True)
-            torch.cuda.synchronize()
-        per = {kn: prof[kn]["ms"] * 1e3 / prof[kn]["launches"] for kn in lr.KERNEL_CLASSES
-               if prof[kn]["launches"]}
+
+        def profiled(flags=0):
+            with lr.Profiler():
+                for i in range(steps):
+                    step(i, flags)
+                prof = lr.Profiler.read(reset=True)
+                torch.cuda.synchronize()
+            return {kn: prof[kn]["ms"] * 1e3 / prof[kn]["launches"] for kn in lr.KERNEL_CLASSES
+                    if prof[kn]["launches"]}
+        per = profiled()
+        # the same steps reusing the plan already in the workspace: the base
+        # GEMM launch without the plan it otherwise carries
+        per_reuse = profiled(lr.FLAG_REUSE_PLAN)
         alg = wl.algorithmic_bytes(w, p)
         shr = per.get("sgmv_shrink", per.get("shrink"))
         exp = per.get("sgmv_expand", per.get("expand"))
-        gemm = per.get("gemm")
+        gemm = per_reuse.get("gemm")
         out[name] = {
             "rows": M, "d": p.d, "k": w.k, "adapter_storage": storage, "n_present": alg["n_present"],
             "adapted_rows": alg["M_a"],
             "tokens_per_s": round(M * steps / el, 1), "ms_per_step": round(el * 1e3 / steps, 4),
             "per_launch_us": {kn: round(v, 2) for kn, v in per.items()},
+            "gemm_us_plan_reused": round(gemm, 2) if gemm else None,
+            "plan_in_gemm_us": round(per["gemm"] - gemm, 2) if gemm and "gemm" in per else None,
             "gemm_tflops": round(alg["gemm_flops"] / gemm / 1e6, 1) if gemm else None,
             "gemm_frac_bf16_peak": round(alg["gemm_flops"] / gemm / 1e6 / BF16_PEAK_TFLOPS, 4) if gemm else None,
             "shrink_gbs": round(alg["shrink_bytes"] / shr / 1e3, 1) if shr else None,

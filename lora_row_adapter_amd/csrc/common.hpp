@@ -38,6 +38,11 @@ enum HdrWord {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Cache-policy bit of buffer accesses: device (agent) scope, coherent across
+// the XCDs' L2 caches.
+constexpr int kCpolSc1 = 16;
 
 // bf16 <-> fp32.  bf16 is the upper half of an fp32; widening is exact.
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

@@ -179,16 +179,15 @@ struct PipeArgs {
   uint64_t epoch;
   int32_t spin_limit;
   int32_t *expired;
-  // split-K pairs: the plan of the layer's batch, run by the first-arriving
-  // workgroup of pair 0 once its partial is out (has_plan != 0)
+  // The plan of the layer's batch: split-K pairs (has_plan != 0) run it in
+  // the first-arriving workgroup of pair 0 once its partial is out; unsplit
+  // tiles (plan_wg != 0) in one workgroup past the tiles, launched where it
+  // fits on a CU beside a tile's workgroup, so it runs alongside the tiles
+  // from the start.
   int32_t has_plan;
+  int32_t plan_wg;
   PlanArgs plan;
 };
-
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-// cache-policy bit of buffer accesses: device (agent) scope, coherent
-// across the XCDs' L2 caches
-constexpr int kCpolSc1 = 16;
 
 // buffer resource over one split-K pair's partial slot
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(uint8_t *slot) {
@@ -264,6 +263,8 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
   constexpr int ECH = (STAGES * STAGE_BYTES >= BM * CLD * 2) ? BM : BM / 2;  // epilogue rows per pass
   static_assert(STAGES * STAGE_BYTES >= ECH * CLD * 2, "epilogue fits");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  static_assert(STAGES * STAGE_BYTES >= plan_detail::plan_sort_lds(plan_detail::kPlanRowBitsMax),
+                "the plan of the largest batch fits the tile's LDS");
   // TX: t column c of this tile's pass p -> (slice << 16 | adapter << 8 |
   // rank) or -1 at [16 p + c]; [32]: the clamped rank sum
   __shared__ int32_t tmap[TX ? 33 : 1];
@@ -273,6 +274,15 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
   // that read one W strip share that XCD's L2
   const int b = blockIdx.x;
   const int ngrid = p.tiles_m * p.tiles_n * SK;
+  if constexpr (SK == 1) {
+    // the extra workgroup, launched only where two of this kernel's
+    // workgroups fit on a CU (its LDS at most half of it): the plan alone
+    constexpr bool kPlanWg = 2 * STAGES * STAGE_BYTES <= 160 * 1024;
+    if (b >= ngrid) {
+      if constexpr (kPlanWg) plan_detail::plan_body<NT>(p.plan, smem, sizeof(smem));
+      return;
+    }
+  }
   const int t = ((ngrid & 7) == 0) ? (b & 7) * (ngrid >> 3) + (b >> 3) : b;
   const int tm = t % p.tiles_m;
   const int ksp = (t / p.tiles_m) % SK;  // k half of a split-K pair
@@ -637,7 +647,7 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       // half finishes the tile -- so the plan needs no kernel, stream or
       // event of its own, and the kernels after the GEMM see it in stream
       // order
-      if (p.has_plan && pair == 0) plan_detail::plan_body<NT>(p.plan, smem, sizeof(smem));
+      if (p.has_plan && pair == 0) plan_detail::plan_body_lean<NT>(p.plan, smem, sizeof(smem));
       return;
     }
     if (tid == 0) {
@@ -843,16 +853,52 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int M, int N, int K, const flo
   }
 }
 
+// Values a launch writes to the split-K pairs' exchange words, one per
+// launch, never 0 (the words' resting value)
+std::atomic<uint64_t> g_epoch{0x9E3779B97F4A7C15ull};
+uint64_t next_epoch() {
+  uint64_t e;
+  do e = g_epoch.fetch_add(1, std::memory_order_relaxed);
+  while (e == 0);
+  return e;
+}
+constexpr int32_t kSpinDefault = 1 << 22;  // polls of ~2 x 64 clocks: ~0.3 s
+std::atomic<int32_t> g_spin_limit{kSpinDefault};
+
+// Whether two workgroups of kernel `fn` (`threads` each) fit on one CU
+// (registers and LDS): then one more workgroup can run the plan beside the
+// tiles.
+bool plan_fits_beside(const void *fn, int threads) {
+  hipFuncAttributes at{};
+  if (!kernel_attributes(fn, &at)) return false;
+  KernelFootprint f;
+  f.threads = threads;
+  f.vgprs = at.numRegs;
+  f.lds = at.sharedSizeBytes;
+  return fits_beside(f, f);
+}
+
+// Returns false when asked to carry a plan it cannot (no launch then).
 template <int BM, int BN, int WM, int WN, int STAGES, bool TX = false>
-void launch_pipe(const PipeArgs &pa0, hipStream_t st) {
+bool launch_pipe(const PipeArgs &pa0, hipStream_t st, const PlanArgs *plan = nullptr) {
   PipeArgs pa = pa0;
   pa.tiles_m = (pa.M + BM - 1) / BM;
   pa.tiles_n = (pa.N + BN - 1) / BN;
   // separate producer waves where the consumers' accumulators leave room
   // for a second wave per SIMD (at most 128 fp32 per lane)
   constexpr bool PC = (BM / WM) * (BN / WN) / 64 <= 128;
-  hipLaunchKernelGGL((k_gemm_bf16_pipe<BM, BN, WM, WN, STAGES, PC, TX>),
-                     dim3(pa.tiles_m * pa.tiles_n), dim3(PC ? 64 * WM * WN + 256 : 256), 0, st, pa);
+  constexpr int threads = PC ? 64 * WM * WN + 256 : 256;
+  const auto fn = k_gemm_bf16_pipe<BM, BN, WM, WN, STAGES, PC, TX>;
+  const int ngrid = pa.tiles_m * pa.tiles_n;
+  int extra = 0;
+  if (plan != nullptr && plan->M > 0) {
+    if (!plan_fits_beside((const void *)fn, threads)) return false;
+    pa.plan = *plan;
+    pa.plan_wg = 1;
+    extra = 1;
+  }
+  hipLaunchKernelGGL(fn, dim3(ngrid + extra), dim3(threads), 0, st, pa);
+  return true;
 }
 
 bool pipe_ok(int64_t k, int64_t ldx, int64_t ldw) {
@@ -928,9 +974,6 @@ bool split_ok(int64_t M, int64_t k, int64_t d, void *gws, size_t gws_bytes) {
   return gws != nullptr && ((uintptr_t)gws & 255u) == 0 && M > 128 && (k % 128) == 0 && k >= 256 &&
          gws_bytes >= split_bytes(M, d);
 }
-std::atomic<uint64_t> g_epoch{0x9E3779B97F4A7C15ull};
-constexpr int32_t kSpinDefault = 1 << 22;  // polls of ~2 x 64 clocks: ~0.3 s
-std::atomic<int32_t> g_spin_limit{kSpinDefault};
 template <bool TX>
 void launch_split(PipeArgs pa, int64_t M, int64_t d, void *gws, int32_t *expired, hipStream_t st,
                   const PlanArgs *plan) {
@@ -946,19 +989,19 @@ void launch_split(PipeArgs pa, int64_t M, int64_t d, void *gws, int32_t *expired
                                          ((size_t)P * kSplitPartBytes + 255) / 256 * 256);
   pa.expired = expired ? expired : reinterpret_cast<int32_t *>(region) + kHdrSyncExpired;
   pa.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  // 0 is the "nobody arrived" value of the pair words
-  pa.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
-  if (pa.epoch == 0) pa.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
+  pa.epoch = next_epoch();
   hipLaunchKernelGGL((k_gemm_bf16_split<144, TX, 2>), dim3(pa.tiles_m * pa.tiles_n * 2), dim3(768),
                      0, st, pa);
 }
 // Unsplit 256 x 160 tiles (e.g. 2048 rows x 5120 columns: 256 tiles, where
 // 256 x 256 tiles leave 96 CUs idle)
-void launch_wide(PipeArgs pa, int64_t M, int64_t d, hipStream_t st) {
+bool launch_wide(PipeArgs pa, int64_t M, int64_t d, hipStream_t st, const PlanArgs *plan) {
+  if (plan != nullptr && plan->M > 0) return false;  // its LDS leaves no room beside it
   pa.tiles_m = (int)((M + 255) / 256);
   pa.tiles_n = (int)((d + 159) / 160);
   hipLaunchKernelGGL((k_gemm_bf16_split<160, false, 1>), dim3(pa.tiles_m * pa.tiles_n), dim3(768),
                      0, st, pa);
+  return true;
 }
 
 }  // namespace
@@ -972,11 +1015,6 @@ void set_sync_spin_limit(int32_t polls) {
   g_spin_limit.store(polls < 0 ? kSpinDefault : polls, std::memory_order_relaxed);
 }
 
-bool gemm_runs_plan(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
-                    void *gws, size_t gws_bytes) {
-  return dtype == 1 && M > 0 && d > 0 && pipe_ok(k, ldx, ldw) && choose_tile(M, d) == 2 &&
-         split_ok(M, k, d, gws, gws_bytes);
-}
 
 hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const void *x, int64_t ldx,
                        const void *W, int64_t ldw, void *y, int64_t ldy, void *gws,
@@ -985,21 +1023,22 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
   if (dtype == 1) {
     if (pipe_ok(k, ldx, ldw)) {
       PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
+      bool ok = true;  // false: asked to carry a plan the launch cannot
       switch (choose_tile(M, d)) {
-        case 0: launch_pipe<256, 256, 2, 2, 2>(pa, st); break;
-        case 1: launch_pipe<256, 128, 4, 1, 3>(pa, st); break;
+        case 0: ok = launch_pipe<256, 256, 2, 2, 2>(pa, st, plan); break;
+        case 1: ok = launch_pipe<256, 128, 4, 1, 3>(pa, st, plan); break;
         case 2:
           if (split_ok(M, k, d, gws, gws_bytes)) {
             launch_split<false>(pa, M, d, gws, expired, st, plan);
           } else {
-            launch_pipe<128, 144, 4, 1, 3>(pa, st);
+            ok = launch_pipe<128, 144, 4, 1, 3>(pa, st, plan);
           }
           break;
-        case 3: launch_pipe<128, 128, 2, 2, 4>(pa, st); break;
-        case 5: launch_wide(pa, M, d, st); break;
-        default: launch_pipe<64, 64, 2, 2, 4>(pa, st); break;
+        case 3: ok = launch_pipe<128, 128, 2, 2, 4>(pa, st, plan); break;
+        case 5: ok = launch_wide(pa, M, d, st, plan); break;
+        default: ok = launch_pipe<64, 64, 2, 2, 4>(pa, st, plan); break;
       }
-      return hipGetLastError();
+      return ok ? hipGetLastError() : hipErrorInvalidValue;
     }
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((d + BN - 1) / BN);
@@ -1077,10 +1116,19 @@ hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int
   pa.ft = ft;
   if (split_ok(M, k, d, gws, gws_bytes)) {
     launch_split<true>(pa, M, d, gws, expired, st, plan);
-  } else {
-    launch_pipe<128, 144, 4, 1, 3, true>(pa, st);
+  } else if (!launch_pipe<128, 144, 4, 1, 3, true>(pa, st, plan)) {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+bool gemm_runs_plan(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
+                    void *gws, size_t gws_bytes, bool fused) {
+  if (dtype != 1 || M <= 0 || d <= 0 || !pipe_ok(k, ldx, ldw)) return false;
+  if (split_ok(M, k, d, gws, gws_bytes) && (fused || choose_tile(M, d) == 2)) return true;
+  KernelFootprint f;
+  return gemm_footprint(dtype, M, k, d, ldx, ldw, gws, gws_bytes, fused, &f) && f.lds > 0 &&
+         fits_beside(f, f) && (fused || choose_tile(M, d) != 5);
 }
 
 }  // namespace lora

@@ -137,12 +137,16 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
                        const void *W, int64_t ldw, void *y, int64_t ldy, void *gws,
                        size_t gws_bytes, hipStream_t st, int32_t *expired = nullptr,
                        const PlanArgs *plan = nullptr);
-// Whether the base GEMM of this shape and GEMM region runs split-K pairs,
-// whose first-arriving workgroup of pair 0 can run the layer's plan.
+// Whether the base GEMM launch of this shape (and GEMM region, and fold)
+// carries the layer's plan: split-K pairs (the first-arriving workgroup of
+// pair 0 runs it), or MFMA tiles whose kernel fits twice on a CU (one more
+// workgroup runs it beside the tiles).  launch_gemm(_fused) with a plan
+// where this is false fails with hipErrorInvalidValue.
 bool gemm_runs_plan(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
-                    void *gws, size_t gws_bytes);
+                    void *gws, size_t gws_bytes, bool fused);
 // Bound of the split-K pairs' wait in polls for later launches (< 0: the
-// default); a test hook that makes every wait expire at once with 0.
+// default); a test hook that makes every wait expire at once with 0 (an
+// expired wait is counted; that tile is wrong).
 void set_sync_spin_limit(int32_t polls);
 // Bytes of GEMM workspace the split-K launch of this shape uses (0: none).
 size_t gemm_ws_bytes(int64_t M, int64_t k, int64_t d);

@@ -624,11 +624,11 @@ lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const
     hipStream_t ps = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     const bool reuse = (flags & LORA_FLAG_REUSE_PLAN) != 0;
-    // Where the base GEMM runs split-K pairs, its first-arriving workgroup
-    // of pair 0 runs the plan (no plan launch, side stream or events: the
-    // fork and join cost ~6.5 us each on the stream at the 70B q+v step)
+    // Where the base GEMM launch can carry the plan, it does (no plan
+    // launch, side stream or events: the fork and join cost ~6.5 us each on
+    // the stream at the 70B q+v step)
     const bool in_gemm = !reuse && !qw &&
-                         gemm_runs_plan(dtype, Mc, k, d_total, ldx, ldw, gws, gws_bytes);
+                         gemm_runs_plan(dtype, Mc, k, d_total, ldx, ldw, gws, gws_bytes, fcap > 0);
     PlanArgs gplan{};
     if (in_gemm) gplan = make_plan_args(Mc, k, dtype, n_slices, slices, adapter_ids + c0, ws, L);
     bool beside = !self_contained && !in_gemm;

@@ -39,11 +39,17 @@ __global__ __launch_bounds__(256) void k_translate(AdapterRef ar, int32_t S, int
 
 }  // namespace
 
-// LDS sized to the batch: the counting sort where its per-wave histograms
-// fit in kMaxLds (with 1024 threads for large batches, else 256), else the
-// bitonic sort (256 threads up to 1024 sort slots, else 1024)
+// LDS sized to the batch: the small-adapter-count plan for up to 64
+// adapters, else the counting sort where its per-wave histograms fit in
+// kMaxLds, else the bitonic sort (each with 1024 threads for batches of more
+// than 1024 rows, else 256)
 static void plan_shape(const PlanArgs &a, size_t kMaxLds, int *nt, size_t *lds) {
   const bool large = (1 << a.row_bits) > 1024;
+  if (a.S <= 64) {
+    *nt = large ? kPlanThreads : 256;
+    *lds = plan_detail::plan_small_lds(a.M, *nt);
+    if (*lds <= kMaxLds) return;
+  }
   const size_t c1024 = plan_detail::plan_count_lds(a.M, a.S, kPlanThreads);
   const size_t c256 = plan_detail::plan_count_lds(a.M, a.S, 256);
   if (large && c1024 <= kMaxLds) {

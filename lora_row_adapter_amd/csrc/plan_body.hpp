@@ -1,5 +1,5 @@
 // plan_body.hpp -- the plan step as a device function, run either by its
-// own kernel or by one extra workgroup of the base GEMM's launch.
+// own kernel or by a workgroup of the base GEMM's launch.
 //
 // Plan ("Adapter Residency When One Replica Serves Many Fine-Tunes", section
 // "Batch composition under many adapters": sort a batch's rows by adapter
@@ -8,7 +8,10 @@
 // corrections run as one segmented operation over the adapter-sorted rows).
 //
 // One workgroup does the whole plan for up to 8192 rows:
-//   1. classify each row (none / adapted / bad id / bad rank / bad page);
+//   1. classify each row (none / adapted / bad id / bad rank / bad page) --
+//      where a table of the adapters fits in LDS, each adapter's ranks and
+//      pages are checked once and the rows' ids (16-byte loads) are looked
+//      up in it;
 //   2. order the adapted rows by (adapter, row) -- a stable counting sort
 //      over the adapters where LDS holds a histogram per wave, else a
 //      bitonic sort of the keys (adapter << row_bits) | row;
@@ -58,21 +61,42 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int *total
   return x - v + wsum[wave];
 }
 
-// Row m's adapter if the row is adapted, else -1; counts the row's class in
-// cnt[0] bad id, cnt[1] bad rank, cnt[2] bad page (rare: counted per row);
-// cnt[3] adapted rows is counted by the callers that need it, per wave.
-__device__ __forceinline__ int plan_classify(const PlanArgs &a, int m, int *cnt) {
-  const int id = a.ids[m];
-  if (id == -1) return -1;  // no adapter
-  if (id < -1 || id >= a.S) {
-    atomicAdd(&cnt[0], 1);
-    return -1;
+// The fields of a slice the row checks read, staged in LDS once per plan
+// (plan_stage_slices): the checks then read them from LDS, and the kernel
+// arguments are read at fixed indexes only, by one thread -- few of them
+// stay live in scalar registers through the plan.
+struct PlanSliceL {
+  const int32_t *ranks;
+  const int32_t *page_table;  // nullptr: slots
+  int64_t n_pages, page_bytes, bytes_per_rank;
+  int32_t R, max_pages;
+};
+__device__ __forceinline__ void plan_stage_slices(const PlanArgs &a, PlanSliceL *sl) {
+  if (threadIdx.x != 0) return;
+#pragma unroll
+  for (int q = 0; q < kMaxSlices; ++q) {
+    if (q >= a.n_slices) break;
+    const PlanSlice &g = a.sl[q];
+    sl[q] = PlanSliceL{g.ranks, g.page_table, g.n_pages, g.page_bytes, g.bytes_per_rank, g.R,
+                       g.max_pages};
   }
+}  // the caller's barrier publishes them
+
+// The class of a row with adapter id `id` whose rank in slice q is rk[q]:
+// the adapter if the row is adapted, else -1 (no adapter), -2 (id outside
+// [-1, S)), -3 (a slice's rank outside [0, R]) or -4 (a slice's pages
+// outside its table or pool).
+__device__ __forceinline__ int plan_class_id(const PlanArgs &a, const PlanSliceL *sls, int id,
+                                             const int rk[kMaxSlices]) {
+  if (id == -1) return -1;  // no adapter
+  if (id < -1 || id >= a.S) return -2;
   // every slice's rank must be in range, then every slice's pages
   bool rank_ok = true, page_ok = true;
-  for (int q = 0; q < a.n_slices; ++q) {
-    const PlanSlice &sl = a.sl[q];
-    const int r = sl.ranks[id];
+#pragma unroll
+  for (int q = 0; q < kMaxSlices; ++q) {
+    if (q >= a.n_slices) break;
+    const PlanSliceL &sl = sls[q];
+    const int r = rk[q];
     if (r < 0 || r > sl.R) {
       rank_ok = false;
       continue;
@@ -87,21 +111,147 @@ __device__ __forceinline__ int plan_classify(const PlanArgs &a, int m, int *cnt)
       }
     }
   }
-  if (!rank_ok) {
-    atomicAdd(&cnt[1], 1);
-    return -1;
-  }
-  if (!page_ok) {
-    atomicAdd(&cnt[2], 1);
-    return -1;
-  }
+  if (!rank_ok) return -3;
+  if (!page_ok) return -4;
   return id;
+}
+
+// The ranks of adapter `id` (taken as adapter 0 outside [0, S)) in every
+// slice.
+__device__ __forceinline__ void plan_ranks_of(const PlanArgs &a, const PlanSliceL *sls, int id,
+                                              int rk[kMaxSlices]) {
+  const int idc = (id >= 0 && id < a.S) ? id : 0;
+#pragma unroll
+  for (int q = 0; q < kMaxSlices; ++q) rk[q] = q < a.n_slices ? sls[q].ranks[idc] : 0;
+}
+
+// Row m's class (plan_class_id).  Without `sls` (the lean plan run inside a
+// GEMM kernel whose registers are spoken for) the slices are walked with a
+// loop over the arguments themselves, one slice's fields live at a time.
+__device__ __forceinline__ int plan_class(const PlanArgs &a, const PlanSliceL *sls, int m) {
+  const int id = a.ids[m];
+  if (sls != nullptr) {
+    int rk[kMaxSlices];
+    plan_ranks_of(a, sls, id, rk);
+    return plan_class_id(a, sls, id, rk);
+  }
+  if (id == -1) return -1;
+  if (id < -1 || id >= a.S) return -2;
+  bool rank_ok = true, page_ok = true;
+  for (int q = 0; q < a.n_slices; ++q) {
+    const PlanSlice &sl = a.sl[q];
+    const int r = sl.ranks[id];
+    if (r < 0 || r > sl.R) {
+      rank_ok = false;
+      continue;
+    }
+    if (sl.page_table != nullptr) {
+      const int64_t pages = ((int64_t)r * sl.bytes_per_rank + sl.page_bytes - 1) / sl.page_bytes;
+      if (pages > sl.max_pages) page_ok = false;
+      for (int64_t j = 0; page_ok && j < pages; ++j) {
+        const int32_t pg = sl.page_table[(int64_t)id * sl.max_pages + j];
+        if (pg < 0 || (int64_t)pg >= sl.n_pages) page_ok = false;
+      }
+    }
+  }
+  return !rank_ok ? -3 : (!page_ok ? -4 : id);
+}
+
+// Row m's adapter if the row is adapted, else -1; a bad row is counted in
+// cnt[0] bad id, cnt[1] bad rank or cnt[2] bad page (rare: counted per
+// row); cnt[3] adapted rows is counted by the callers, per wave.  With
+// `cls` the class is read from cls[m] (LDS, plan_classes), else found here.
+__device__ __forceinline__ int plan_row(const PlanArgs &a, const PlanSliceL *sls, const int *cls,
+                                        int m, int *cnt) {
+  const int c = cls ? cls[m] : plan_class(a, sls, m);
+  if (c < -1) {
+    atomicAdd(&cnt[min(-2 - c, 2)], 1);
+    return -1;
+  }
+  return c;
+}
+
+// Validity of every adapter into vt[0, S) (LDS bytes): 0 when each slice's
+// rank of the adapter is in [0, R] and its pages lie in the table and the
+// pool, 1 for a bad rank, 2 for a bad page, so a row's class follows from its
+// id alone (plan_class_vt).  U adapters per thread at a time: their ranks in
+// every slice are loaded before the first is waited for.
+template <int NT, int U>
+__device__ __forceinline__ void plan_validate(const PlanArgs &a, const PlanSliceL *sls, int8_t *vt) {
+  for (int base = threadIdx.x; base < a.S; base += NT * U) {
+    int rk[U][kMaxSlices];
+#pragma unroll
+    for (int u = 0; u < U; ++u) plan_ranks_of(a, sls, min(base + NT * u, a.S - 1), rk[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = base + NT * u;
+      if (s < a.S) {
+        const int c = plan_class_id(a, sls, s, rk[u]);  // s, -3 or -4
+        vt[s] = (int8_t)(c >= 0 ? 0 : -2 - c);
+      }
+    }
+  }
+}
+
+// plan_class of a row with adapter id `id`, from the validity table.
+__device__ __forceinline__ int plan_class_vt(int id, int S, const int8_t *vt) {
+  if (id == -1) return -1;
+  if (id < -1 || id >= S) return -2;
+  const int v = vt[id];
+  return v == 0 ? id : -2 - v;
+}
+
+// The classes of all M rows into cls[0, M) (LDS, int or int8_t entries;
+// room for M rounded up to 4): the ids are read with 16-byte buffer loads
+// (four per thread issued before the first is waited for; the buffer's bound
+// turns reads past the last row into zeros, which are not stored), and the
+// validity table vt (LDS, S bytes) is built while the first of them are in
+// flight.  Ends with a barrier.
+template <int NT, typename C>
+__device__ __forceinline__ void plan_classes(const PlanArgs &a, const PlanSliceL *sls, int8_t *vt,
+                                             C *cls) {
+  constexpr int U = 4;
+  const int M = a.M;
+  const int n16 = (M + 3) / 4;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(a.ids), 0, M * 4, 0x00020000);
+  u32x4_t v[U];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = __builtin_bit_cast(u32x4_t,
+                                __builtin_amdgcn_raw_buffer_load_b128(rs, (c0 + u * NT) * 16, 0, 0));
+  };
+  load(threadIdx.x);
+  plan_validate<NT, 2>(a, sls, vt);
+  __syncthreads();
+  for (int c0 = threadIdx.x; c0 < n16; c0 += NT * U) {
+    if (c0 != (int)threadIdx.x) load(c0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int m = 4 * (c0 + u * NT);
+      if (m >= M) continue;
+      int c[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = m + e < M ? plan_class_vt((int)v[u][e], a.S, vt) : -1;
+      if constexpr (sizeof(C) == 1) {
+        *reinterpret_cast<uint32_t *>(cls + m) = (uint32_t)(c[0] & 0xff) | (uint32_t)(c[1] & 0xff) << 8 |
+                                                 (uint32_t)(c[2] & 0xff) << 16 | (uint32_t)c[3] << 24;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (m + e < M) cls[m + e] = c[e];
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // Bitonic plan.  `plan_lds` holds plan_sort_lds(row_bits) bytes: the sort
 // keys [n2] then segment starts [n2] (uint16).
 template <int NT>
-__device__ __forceinline__ void plan_bitonic(const PlanArgs &a, uint8_t *plan_lds) {
+__device__ __forceinline__ void plan_bitonic(const PlanArgs &a, const PlanSliceL *sls,
+                                             uint8_t *plan_lds) {
   uint32_t *keys = reinterpret_cast<uint32_t *>(plan_lds);
   uint16_t *sstart = reinterpret_cast<uint16_t *>(plan_lds + ((size_t)4 << a.row_bits));
   __shared__ int wsum[32];
@@ -127,7 +277,7 @@ __device__ __forceinline__ void plan_bitonic(const PlanArgs &a, uint8_t *plan_ld
   for (int m = tid; m < n2; m += NT) {
     uint32_t key = kSentinel;
     if (m < M) {
-      const int id = plan_classify(a, m, cnt);
+      const int id = plan_row(a, sls, nullptr, m, cnt);
       if (id >= 0) key = ((uint32_t)id << a.row_bits) | (uint32_t)m;
     }
     const uint64_t valid = __ballot(key != kSentinel);
@@ -198,7 +348,8 @@ __device__ __forceinline__ void plan_bitonic(const PlanArgs &a, uint8_t *plan_ld
     const int ad = (int)(keys[st] >> a.row_bits);
     int rk[kMaxSlices];
 #pragma unroll
-    for (int q = 0; q < kMaxSlices; ++q) rk[q] = q < a.n_slices ? a.sl[q].ranks[ad] : 0;
+    for (int q = 0; q < kMaxSlices; ++q)
+      rk[q] = q < a.n_slices ? (sls ? sls[q].ranks[ad] : a.sl[q].ranks[ad]) : 0;
     for (int p = 0; p < len; p += kRowsPerGatherItem) {
       Item it;
       it.adapter = ad;
@@ -237,19 +388,23 @@ __device__ __forceinline__ void plan_bitonic(const PlanArgs &a, uint8_t *plan_ld
 // LDS bytes of each form of the plan.
 __host__ __device__ constexpr size_t plan_align16(size_t v) { return (v + 15) & ~(size_t)15; }
 __host__ __device__ constexpr size_t plan_sort_lds(int row_bits) { return (size_t)6 << row_bits; }
+constexpr int kPlanRowBitsMax = 13;  // sort width of the largest batch
+static_assert((1 << kPlanRowBitsMax) == kPlanMaxRows, "kPlanMaxRows rows");
 __host__ __device__ constexpr size_t plan_count_lds(int M, int S, int NT) {
-  return plan_align16((size_t)M * 4) + plan_align16((size_t)S * 4) * (2 + NT / 64);
+  return plan_align16((size_t)M * 4) + plan_align16((size_t)S * 4) * (2 + NT / 64) +
+         plan_align16((size_t)S);
 }
 
 // Counting-sort plan.  `lds` holds plan_count_lds(M, S, NT) bytes: the
-// rows' adapters [M], a histogram [S] (then each adapter's first sorted
-// position), each adapter's first gather item [S] and per-wave counts
-// [NT / 64][S].
+// rows' classes, then adapters [M], a histogram [S] (then each adapter's
+// first sorted position), each adapter's first gather item [S], per-wave
+// counts [NT / 64][S] and the adapters' validity table [S] (bytes).
 // Wave w owns the rows [w * RPW, (w + 1) * RPW): the per-wave counts give
 // each (wave, adapter) its first sorted position, and the wave then places
 // its rows in row order, so equal adapters keep row order (stable).
 template <int NT>
-__device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
+__device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSliceL *sls,
+                                              uint8_t *lds) {
   constexpr int NW = NT / 64;
   __shared__ int wsum[32];
   __shared__ int cnt[4];
@@ -263,6 +418,7 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
   int *hist = reinterpret_cast<int *>(lds + plan_align16((size_t)M * 4));
   int *ibase = hist + plan_align16((size_t)S * 4) / 4;
   int *cntw = ibase + plan_align16((size_t)S * 4) / 4;
+  int8_t *vt = reinterpret_cast<int8_t *>(cntw + plan_align16((size_t)S * 4) / 4 * NW);
   int32_t *hdr = reinterpret_cast<int32_t *>(a.ws + a.L.hdr);
   int32_t *perm = reinterpret_cast<int32_t *>(a.ws + a.L.perm);
   int32_t *seg_adapter = reinterpret_cast<int32_t *>(a.ws + a.L.seg_adapter);
@@ -276,7 +432,10 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
   if (tid < 4) cnt[tid] = 0;
   for (int s = tid; s < S; s += NT) hist[s] = 0;
   for (int i = tid; i < NW * S; i += NT) cntw[i] = 0;
-  __syncthreads();
+  if (sls != nullptr)
+    plan_classes<NT>(a, sls, vt, binv);  // ends with a barrier
+  else
+    __syncthreads();
 
   // 1. classify; histogram per adapter and per (wave range, adapter).  The
   //    64 rows a wave classifies at once lie in one wave range (RPW is a
@@ -285,7 +444,7 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
   //    serialized: 24 us for 8192 rows of 8 adapters)
   for (int mb = wave * 64; mb < M; mb += NT) {
     const int m = mb + lane;
-    const int b = m < M ? plan_classify(a, m, cnt) : -1;
+    const int b = m < M ? plan_row(a, sls, sls ? binv : nullptr, m, cnt) : -1;
     if (m < M) binv[m] = b;
     const int wr = mb / RPW;
     uint64_t pending = __ballot(b >= 0);
@@ -330,7 +489,8 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
       seg_len[oseg] = h;
       int rk[kMaxSlices];
 #pragma unroll
-      for (int q = 0; q < kMaxSlices; ++q) rk[q] = q < a.n_slices ? a.sl[q].ranks[s] : 0;
+      for (int q = 0; q < kMaxSlices; ++q)
+        rk[q] = q < a.n_slices ? (sls ? sls[q].ranks[s] : a.sl[q].ranks[s]) : 0;
       for (int p = 0; p < h; p += kRowsPerGatherItem) {
         Item it;
         it.adapter = s;
@@ -404,14 +564,307 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, uint8_t *lds) {
   }
 }
 
+// Byte i of a packed class word, sign-extended.
+__device__ __forceinline__ int plan_cls_byte(uint32_t w, int i) {
+  return (int)(w << (24 - 8 * i)) >> 24;
+}
+
+// Plan for batches of at most 64 adapters, where one wave holds a value per
+// adapter (lane s: adapter s).  `lds` holds plan_small_lds(M, NT) bytes: the
+// row classes [M] (bytes), the sorted rows [M + 16], the rows of each
+// adapter in each wave's row range [NW][64], per-adapter tables [9][64] and
+// the adapters' validity [64] (bytes).
+//   0. the classes of all rows (plan_classes);
+//   A. each wave takes a contiguous range of rows (RPW, whole blocks of
+//      64 * RL rows, RL consecutive rows per lane: 4 where every wave has
+//      whole blocks, so a long run of one adapter takes a quarter of the
+//      steps, else 1, so short ranges of many adapters spread over all
+//      waves) and counts them per adapter with RL ballots per distinct
+//      adapter of a block, into lane s's register;
+//   B. wave 0: per adapter the row total, its first sorted position, first
+//      16- and 64-row work items and segment (four wave-wide exclusive
+//      scans, run side by side), the first position of each wave's rows,
+//      the segment table, and the adapter's rank in every slice;
+//   C. each wave walks its range again: the rows of adapter s in a block
+//      take consecutive positions after the wave's running offset (a
+//      register of lane s, read with readlane and moved on by lane s), and
+//      are written to the sorted rows in LDS;
+//   D. every thread copies the sorted rows out to perm with 16-byte stores,
+//      and the waves write the work items, adapter by adapter, each item's
+//      rows read back from LDS -- 16-byte stores throughout, instead of
+//      scattered 4-byte stores per row and adapter.
+// Stable by construction: the waves' ranges are in row order, and so are a
+// block's rows in (lane, row) order.  No LDS atomics except the rare bad-row
+// counts.
+__host__ __device__ constexpr size_t plan_small_lds(int M, int NT) {
+  return plan_align16((size_t)M) + plan_align16((size_t)(M + 16) * 4) + (size_t)(NT / 64) * 64 * 4 +
+         9 * 64 * 4 + 64;
+}
+
+template <int NT, int RL>
+__device__ __forceinline__ void plan_small(const PlanArgs &a, const PlanSliceL *sls, uint8_t *lds) {
+  static_assert(RL == 1 || RL == 4, "1 or 4 rows per lane");
+  constexpr int NW = NT / 64;
+  static_assert(kMaxSlices == 4, "four rank columns in the tables");
+  static_assert(kRowsPerGatherItem == 16 && kRowsPerSgmvItem % 16 == 0, "16-row item rows");
+  static_assert(sizeof(Item) == 16 && sizeof(ItemRows) == 80 && offsetof(ItemRows, rows) == 16,
+                "items, their rank columns and rows are written as 16-byte stores");
+  __shared__ int cnt[4];   // bad ids, bad ranks, bad pages
+  __shared__ int tot[4];   // adapted rows, 16-row items, 64-row items, segments
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int M = a.M;
+  const int S = a.S;
+  int8_t *cls = reinterpret_cast<int8_t *>(lds);
+  int *permL = reinterpret_cast<int *>(lds + plan_align16((size_t)M));
+  int *cntw = reinterpret_cast<int *>(lds + plan_align16((size_t)M) + plan_align16((size_t)(M + 16) * 4));
+  // per adapter: [0] first sorted position [64] first 16-row item [128]
+  // first 64-row item [192] rows [256] segment [320 + 64 q] rank in slice q
+  int *tab = cntw + NW * 64;
+  int8_t *vt = reinterpret_cast<int8_t *>(tab + 9 * 64);
+  int32_t *hdr = reinterpret_cast<int32_t *>(a.ws + a.L.hdr);
+  int32_t *perm = reinterpret_cast<int32_t *>(a.ws + a.L.perm);
+  int32_t *seg_adapter = reinterpret_cast<int32_t *>(a.ws + a.L.seg_adapter);
+  int32_t *seg_start = reinterpret_cast<int32_t *>(a.ws + a.L.seg_start);
+  int32_t *seg_len = reinterpret_cast<int32_t *>(a.ws + a.L.seg_len);
+  Item *items_g = reinterpret_cast<Item *>(a.ws + a.L.items_g);
+  ItemRows *items_gx = reinterpret_cast<ItemRows *>(a.ws + a.L.items_gx);
+  Item *items_s = reinterpret_cast<Item *>(a.ws + a.L.items_s);
+  constexpr int BLK = 64 * RL;  // rows per block
+  const int RPW = ((M + NW - 1) / NW + BLK - 1) / BLK * BLK;
+  const int r0 = min(M, wave * RPW);
+  const int r1 = min(M, r0 + RPW);
+
+  // wave 0 loads the ranks of adapter `lane` first: their latency overlaps A
+  int rk[kMaxSlices];
+#pragma unroll
+  for (int q = 0; q < kMaxSlices; ++q)
+    rk[q] = (wave == 0 && q < a.n_slices && lane < S) ? sls[q].ranks[lane] : 0;
+
+  if (tid < 4) cnt[tid] = 0;
+  plan_classes<NT>(a, sls, vt, cls);  // ends with a barrier
+
+  // this lane's RL rows of the block at `base`: classes, -1 past r1
+  auto block = [&](int base, int c[RL]) {
+    const int m0 = base + RL * lane;
+    if constexpr (RL == 4) {
+      const uint32_t w = m0 < r1 ? *reinterpret_cast<const uint32_t *>(cls + m0) : 0xffffffffu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = m0 + i < r1 ? plan_cls_byte(w, i) : -1;
+    } else {
+      c[0] = m0 < r1 ? (int)cls[m0] : -1;
+    }
+  };
+  // first class >= 0 among c[0..RL) (-1 if none)
+  auto first_of = [](const int c[RL]) {
+    int f = c[RL - 1];
+#pragma unroll
+    for (int i = RL - 2; i >= 0; --i) f = c[i] >= 0 ? c[i] : f;
+    return f;
+  };
+
+  // A. per-adapter counts of this wave's range; bad rows become -1
+  int mine = 0;
+  for (int base = r0; base < r1; base += BLK) {
+    int c[RL];
+    block(base, c);
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < RL; ++i) bad = bad || c[i] < -1;
+    if (bad) {  // rare: count, and store the rows as unadapted
+#pragma unroll
+      for (int i = 0; i < RL; ++i) {
+        if (c[i] < -1) {
+          atomicAdd(&cnt[min(-2 - c[i], 2)], 1);
+          c[i] = -1;
+          cls[base + RL * lane + i] = -1;
+        }
+      }
+    }
+    for (;;) {
+      const int f = first_of(c);
+      const uint64_t pf = __ballot(f >= 0);
+      if (pf == 0) break;
+      const int s = __builtin_amdgcn_readlane(f, __ffsll((unsigned long long)pf) - 1);
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < RL; ++i) {
+        n += __popcll(__ballot(c[i] == s));
+        if (c[i] == s) c[i] = -1;
+      }
+      if (lane == s) mine += n;
+    }
+  }
+  cntw[wave * 64 + lane] = mine;
+  __syncthreads();
+
+  // B. per adapter (wave 0, lane s)
+  if (wave == 0) {
+    int h = 0;
+    for (int w = 0; w < NW; ++w) h += cntw[w * 64 + lane];
+    const int v[4] = {h, (h + kRowsPerGatherItem - 1) / kRowsPerGatherItem,
+                      (h + kRowsPerSgmvItem - 1) / kRowsPerSgmvItem, h > 0 ? 1 : 0};
+    int inc[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = __shfl_up(inc[i], o, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane >= o) inc[i] += y[i];
+    }
+    const int start = inc[0] - v[0];
+    const int seg = inc[3] - v[3];
+    int run = start;
+    for (int w = 0; w < NW; ++w) {
+      const int c = cntw[w * 64 + lane];
+      cntw[w * 64 + lane] = run;
+      run += c;
+    }
+    tab[lane] = start;
+    tab[64 + lane] = inc[1] - v[1];
+    tab[128 + lane] = inc[2] - v[2];
+    tab[192 + lane] = h;
+    tab[256 + lane] = seg;
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) tab[320 + 64 * q + lane] = rk[q];
+    if (h > 0) {
+      seg_adapter[seg] = lane;
+      seg_start[seg] = start;
+      seg_len[seg] = h;
+    }
+    if (lane == 63) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[i] = inc[i];
+    }
+  }
+  __syncthreads();
+
+  // C. sorted positions into LDS
+  {
+    int off = cntw[wave * 64 + lane];
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int base = r0; base < r1; base += BLK) {
+      int c[RL];
+      block(base, c);
+      int pos[RL];
+      bool valid[RL];
+#pragma unroll
+      for (int i = 0; i < RL; ++i) {
+        pos[i] = 0;
+        valid[i] = c[i] >= 0;
+      }
+      for (;;) {
+        const int f = first_of(c);
+        const uint64_t pf = __ballot(f >= 0);
+        if (pf == 0) break;
+        const int s = __builtin_amdgcn_readlane(f, __ffsll((unsigned long long)pf) - 1);
+        uint64_t mk[RL];
+        int before = 0, n = 0;
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+          mk[i] = __ballot(c[i] == s);
+          before += __popcll(mk[i] & below);
+          n += __popcll(mk[i]);
+        }
+        const int first = __builtin_amdgcn_readlane(off, s) + before;
+        int k = 0;
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+          if (c[i] == s) {
+            pos[i] = first + k++;
+            c[i] = -1;
+          }
+        }
+        if (lane == s) off += n;
+      }
+#pragma unroll
+      for (int i = 0; i < RL; ++i)
+        if (valid[i]) permL[pos[i]] = base + RL * lane + i;
+    }
+  }
+  __syncthreads();
+
+  // D. perm and the work items, with 16-byte stores
+  const int n_ad = tot[0];
+  for (int e = 4 * tid; e < n_ad; e += 4 * NT) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(permL + e);
+    if (e + 3 < n_ad) {
+      *reinterpret_cast<u32x4_t *>(perm + e) = v;
+    } else {
+      for (int i = 0; i < 4 && e + i < n_ad; ++i) perm[e + i] = (int)v[i];
+    }
+  }
+  for (int s = wave; s < S; s += NW) {
+    const int h = tab[192 + s];
+    if (h == 0) continue;
+    const int start = tab[s], ib = tab[64 + s], sb = tab[128 + s], seg = tab[256 + s];
+    const u32x4_t r = {(unsigned)tab[320 + s], (unsigned)tab[384 + s], (unsigned)tab[448 + s],
+                       (unsigned)tab[512 + s]};
+    for (int j = lane; j * kRowsPerGatherItem < h; j += 64) {
+      const int rel = j * kRowsPerGatherItem;
+      const u32x4_t it = {(unsigned)s, (unsigned)(start + rel),
+                          (unsigned)min(kRowsPerGatherItem, h - rel), (unsigned)seg};
+      *reinterpret_cast<u32x4_t *>(items_g + ib + j) = it;
+      u32x4_t *dst = reinterpret_cast<u32x4_t *>(items_gx + ib + j);
+      dst[0] = r;
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const int *src = permL + start + rel + 4 * b4;  // past the segment: unused entries
+        dst[1 + b4] = u32x4_t{(unsigned)src[0], (unsigned)src[1], (unsigned)src[2], (unsigned)src[3]};
+      }
+    }
+    for (int j = lane; j * kRowsPerSgmvItem < h; j += 64) {
+      const int rel = j * kRowsPerSgmvItem;
+      const u32x4_t it = {(unsigned)s, (unsigned)(start + rel),
+                          (unsigned)min(kRowsPerSgmvItem, h - rel), (unsigned)seg};
+      *reinterpret_cast<u32x4_t *>(items_s + sb + j) = it;
+    }
+  }
+
+  if (tid == 0) {
+    hdr[kHdrBadIds] = cnt[0];
+    hdr[kHdrBadRanks] = cnt[1];
+    hdr[kHdrBadPages] = cnt[2];
+    hdr[kHdrAdapted] = n_ad;
+    hdr[kHdrSegments] = tot[3];
+    hdr[kHdrItemsGather] = tot[1];
+    hdr[kHdrItemsSgmv] = tot[2];
+    hdr[kHdrRows] = M;
+  }
+}
+
 // The whole plan, run by one workgroup of NT threads, in `lds_bytes` of LDS
 // at `lds` (the caller guarantees room for at least the bitonic form).
 template <int NT>
 __device__ __forceinline__ void plan_body(const PlanArgs &a, uint8_t *lds, size_t lds_bytes) {
+  __shared__ PlanSliceL sls[kMaxSlices];
+  plan_stage_slices(a, sls);
+  __syncthreads();
+  if (a.S <= 64 && plan_small_lds(a.M, NT) <= lds_bytes) {
+    if (a.M >= NT * 4)  // every wave has whole blocks of 256 rows
+      plan_small<NT, 4>(a, sls, lds);
+    else
+      plan_small<NT, 1>(a, sls, lds);
+  } else if (plan_count_lds(a.M, a.S, NT) <= lds_bytes) {
+    plan_counting<NT>(a, sls, lds);
+  } else {
+    plan_bitonic<NT>(a, sls, lds);
+  }
+}
+
+// The lean plan, for a workgroup of a GEMM kernel whose registers its own
+// loop has spoken for: the counting or bitonic sort with each row's class
+// found on its own (the slices walked with a loop), so the plan adds little
+// register pressure to the kernel.
+template <int NT>
+__device__ __forceinline__ void plan_body_lean(const PlanArgs &a, uint8_t *lds, size_t lds_bytes) {
   if (plan_count_lds(a.M, a.S, NT) <= lds_bytes)
-    plan_counting<NT>(a, lds);
+    plan_counting<NT>(a, nullptr, lds);
   else
-    plan_bitonic<NT>(a, lds);
+    plan_bitonic<NT>(a, nullptr, lds);
 }
 
 }  // namespace plan_detail
