@@ -184,10 +184,15 @@ lora_status_t lora_gemm(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, con
  * segment and work-item tables), base GEMM y = x W^T, shrink t = x A_s^T
  * over k into fp32 partials (one per k split), expand y += scale_s t B_s^T
  * on adapted rows only (t = the partials summed in split order).  All run
- * on `stream` except the plan, which the library runs on its own side
- * stream (one per device, default priority) beside the GEMM, joined by an
- * event before the shrink; from the caller's view the call is ordered on
- * `stream` as usual.  Rows with no adapter are written once, by the GEMM.
+ * on `stream`.  The plan rides inside the base GEMM's launch where that
+ * launch can carry it without slowing its tiles (split-K workgroup pairs:
+ * the first to arrive runs it; tiles whose kernel fits twice on a CU: one
+ * extra workgroup runs it beside them); otherwise it is its own kernel,
+ * beside the GEMM on the library's side stream (one per device, default
+ * priority, joined by an event before the shrink) where one of its
+ * workgroups fits on a CU next to one of the GEMM's, else on `stream` ahead
+ * of the GEMM.  From the caller's view the call is ordered on `stream` as
+ * usual.  Rows with no adapter are written once, by the GEMM.
  * Results are run-to-run deterministic (no floating-point atomics).
  */
 lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, const void *x,
@@ -251,8 +256,9 @@ lora_status_t lora_linear_sliced(lora_dtype_t dtype, int64_t M, int64_t k, const
  *     whose workspace need (lora_workspace_bytes_sliced) exceeds it returns
  *     LORA_ERR_WORKSPACE and launches nothing;
  *   - the call allocates nothing (no hipMalloc / hipFree, no stream or event
- *     creation): the plan runs on `stream` ahead of the base GEMM, not beside
- *     it, and launches are not timed by lora_profile_*;
+ *     creation): the plan runs inside the base GEMM's launch where it can,
+ *     else on `stream` ahead of the GEMM (never on the side stream), and
+ *     launches are not timed by lora_profile_*;
  *   - every call on one GPU shares that GPU's array and its contents stay
  *     from the last call: calls that overlap on one GPU (two streams, two
  *     threads) race, so the caller serialises them; LORA_FLAG_REUSE_PLAN
