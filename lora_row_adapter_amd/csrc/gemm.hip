@@ -255,11 +255,11 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
   constexpr int A_BYTES = BM * BKB;
   constexpr int STAGE_BYTES = (BM + BROWS) * BKB;
   constexpr int FM = BM / WM / 16;
-  constexpr int FN = BN / WN / 16 + (TX ? 1 : 0);        // TX: + the t block
-  constexpr int FNY = BN / WN / 16;                      // blocks that go to y
+  // TX: the t block is the last 16-column block of the last wave column
+  constexpr int FN = (BN + (TX ? 16 : 0)) / WN / 16;
   constexpr int CLD = BN + 8;                            // epilogue LDS row (bf16)
-  static_assert(FM * WM * 16 == BM && FNY * WN * 16 == BN, "tile split");
-  static_assert(!TX || (PC && WN == 1 && BROWS - BN == 16), "t rows fill the W stage's padding");
+  static_assert(FM * WM * 16 == BM && FN * WN * 16 == BN + (TX ? 16 : 0), "tile split");
+  static_assert(!TX || (PC && BROWS - BN == 16), "t rows fill the W stage's padding");
   constexpr int ECH = (STAGES * STAGE_BYTES >= BM * CLD * 2) ? BM : BM / 2;  // epilogue rows per pass
   static_assert(STAGES * STAGE_BYTES >= ECH * CLD * 2, "epilogue fits");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
@@ -417,7 +417,9 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int wm0 = (pw / WN) * (FM * 16);
-  const int wn0 = (pw % WN) * (FNY * 16);
+  const int wn0 = (pw % WN) * (FN * 16);
+  // TX: whether this wave's last column block is the t block (uniform)
+  const bool t_wave = TX && (pw % WN) == WN - 1;
 
   // one k32 step: fragments of this wave's rows and of every column block
   // (one base offset per operand, the blocks at immediate offsets), then
@@ -681,15 +683,21 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
   if constexpr (TX) {
     // t: this tile's rows x its 16 t columns, kept where the row's adapter
     // owns the column (tmap was written before the k loop's barriers)
-    if (owner) {
+    if (owner && t_wave) {
       const FusedT &ft = p.ft;
       // the rows' ids first (one batch of loads at clamped rows)
-      int id[FM][4];
+      // (two per register: ids outside [0, 256) -- none or invalid, never
+      // an adapter of the map -- as 0xFFFF)
+      uint32_t id2[FM][2];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          id[i][e] = ft.ids[min(m0 + wm0 + i * 16 + ((lane >> 4) << 2) + e, p.M - 1)];
+        for (int e = 0; e < 4; e += 2) {
+          const int r = m0 + wm0 + i * 16 + ((lane >> 4) << 2) + e;
+          const uint32_t lo = (uint32_t)ft.ids[min(r, p.M - 1)];
+          const uint32_t hi = (uint32_t)ft.ids[min(r + 1, p.M - 1)];
+          id2[i][e >> 1] = (lo < 256u ? lo : 0xFFFFu) | ((hi < 256u ? hi : 0xFFFFu) << 16);
+        }
       auto scatter = [&](int v, const f32x4_t (&t)[FM]) {
         if (v < 0) return;
         const int q = v >> 16, a = (v >> 8) & 255, j = v & 255;
@@ -698,7 +706,7 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = m0 + wm0 + i * 16 + ((lane >> 4) << 2) + e;
-            if (m < p.M && id[i][e] == a)
+            if (m < p.M && ((id2[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu) == (uint32_t)a)
               ft.tpart[((int64_t)m * ft.n_slices + q) * ft.Rw + j] = t[i][e];
           }
       };
@@ -722,20 +730,14 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
         f32x4_t t1[FM];
 #pragma unroll
         for (int i = 0; i < FM; ++i) t1[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < p.K; k0 += 64) {  // K % 64 == 0
-          bf16x8_t xf[2][FM], af[2];
+        for (int k0 = 0; k0 < p.K; k0 += 32) {  // K % 64 == 0
+          bf16x8_t xf[FM];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int i = 0; i < FM; ++i) xf[i] = *reinterpret_cast<const bf16x8_t *>(xr[i] + k0);
+          const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(asrc + k0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-              xf[u][i] = *reinterpret_cast<const bf16x8_t *>(xr[i] + k0 + 32 * u);
-            af[u] = *reinterpret_cast<const bf16x8_t *>(asrc + k0 + 32 * u);
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-              t1[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][i], af[u], t1[i], 0, 0, 0);
+          for (int i = 0; i < FM; ++i)
+            t1[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i], af, t1[i], 0, 0, 0);
         }
         scatter(v1, t1);
       }
@@ -753,7 +755,8 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       const int rb = wm0 + i * 16;
       if (!owner || rb < r0 || rb >= r0 + ECH) continue;
 #pragma unroll
-      for (int j = 0; j < FNY; ++j) {
+      for (int j = 0; j < FN; ++j) {
+        if (TX && j == FN - 1 && t_wave) continue;
         const f32x4_t v = tile_val(i, j);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -792,13 +795,20 @@ __global__ __launch_bounds__(PC ? 64 * WM * WN + 256 : 256) void k_gemm_bf16_pip
   pipe_body<BM, BN, WM, WN, STAGES, PC, TX, 1>(p);
 }
 
-// 256-row tiles with eight MFMA waves (32 x BN each) beside the four
-// producers: split-K pairs (SK = 2) over 256 x 144 tiles, and unsplit
-// 256 x 160 tiles.  At most 160 VGPRs, so three waves per SIMD leave room for
-// the plan kernel (32 VGPRs) that the layer runs beside the GEMM.
+// 256-row tiles with eight MFMA waves beside the four producers: split-K
+// pairs (SK = 2) over 256 x 144 tiles, and unsplit 256 x 160 tiles.  Where
+// the W stage's rows (with the folded shrink's 16) split into two 16-column
+// multiples, the waves take 64 x (rows / 2) each (4 x 2), else 32 x 144
+// (8 x 1): per k step a wave reads (M_w + N_w) fragment rows for M_w x N_w
+// outputs, so the 4 x 2 split reads 25% fewer LDS bytes per flop (measured
+// at the 70B q+v shape with the shrink folded in: 85.4 -> 82.7 us).
+#ifndef LORA_SPLIT_WN
+#define LORA_SPLIT_WN 2
+#endif
 template <int BN, bool TX, int SK>
 __global__ __launch_bounds__(768) void k_gemm_bf16_split(PipeArgs p) {
-  pipe_body<256, BN, 8, 1, 3, true, TX, SK>(p);
+  constexpr int WN = ((BN + (TX ? 16 : 0)) % 32 == 0) ? LORA_SPLIT_WN : 1;
+  pipe_body<256, BN, 8 / WN, WN, 3, true, TX, SK>(p);
 }
 
 constexpr int FBM = 64, FBN = 64, FBK = 16;
