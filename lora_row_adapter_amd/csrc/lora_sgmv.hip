@@ -36,6 +36,24 @@ namespace lora {
 namespace {
 
 constexpr int RMAX_MFMA = 64; // largest max_rank these kernels take
+#ifndef LORA_SS16_16
+#define LORA_SS16_16 3
+#endif
+#ifndef LORA_SS16_32
+#define LORA_SS16_32 3
+#endif
+#ifndef LORA_SS16_64
+#define LORA_SS16_64 3
+#endif
+#ifndef LORA_SS64_16
+#define LORA_SS64_16 5
+#endif
+#ifndef LORA_SS64_32
+#define LORA_SS64_32 4
+#endif
+#ifndef LORA_SS64_64
+#define LORA_SS64_64 4
+#endif
 constexpr int kExpandCols16 = 256;  // expand columns per workgroup, 16-row items (512 measured slower)
 
 __device__ __forceinline__ bf16x8_t ld16(const void *p) {
@@ -864,11 +882,243 @@ void expand_pick(const LoraArgs &a, int mode, bool r32, dim3 grid, hipStream_t s
   else expand_mode<RB, RMAX_MFMA>(a, mode, grid, st);
 }
 
+// ---------------------------------------------------------------------------
+// Shrink over LDS-staged operand tiles (one slice per workgroup, at most 4
+// rank blocks).  A load instruction that gives each of 16 rows 64 bytes
+// (the MFMA operand layout read straight from memory) streams gathered rows
+// at ~3.3 TB/s; whole 128-byte row segments stream at twice that.  So the
+// item's x rows and the adapter's A rows go to a ring of LDS stages as
+// 8 rows x 128 bytes per instruction (buffer_load / global_load ... lds:
+// lane l's 16 bytes land at the instruction's LDS base + 16 l; chunk c of a
+// row is stored at c ^ (row & 7), so the 16 lanes that read one fragment
+// column hit distinct banks), STAGES - 1 k-tiles of 64 in flight, and the
+// fragments are read back with ds_read_b128.  All four waves issue loads
+// (each the same count per stage, padded with loads that write zeros to a
+// scratch block, so one vmcnt bound covers every wave); one barrier per
+// k-tile.  64-row items: wave w owns row block w and every rank block; 16-row
+// items: wave w owns rank block w.  The outputs are disjoint, so no
+// cross-wave sum.  Same fp32 partials as k_shrink_mfma.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void shrink_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// wait until at most n (uniform, 0 <= n <= N) vector memory ops are in flight
+template <int N>
+__device__ __forceinline__ void shrink_wait_le(int n) {
+  if constexpr (N == 0) {
+    shrink_wait_vmcnt<0>();
+  } else {
+    if (n >= N) shrink_wait_vmcnt<N>();
+    else shrink_wait_le<N - 1>(n);
+  }
+}
+
+// 16 bytes per lane from base + off into LDS (lane l at lds + 16 l); an
+// offset at or past nbytes writes zeros and reads nothing (the range check
+// is per dword against nbytes, so nbytes must stay below the pad offset
+// 0xFFFFFFF0 for those loads to read nothing).  (Not a template: the
+// buffer-resource type exists only in device compilation.)
+__device__ __forceinline__ void x_load_lds(const void *base, uint32_t nbytes, void *lds, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off,
+                                           0, 0, 0);
+}
+
+// 16 bytes per lane from the lane's own address into LDS (lane l at lds + 16 l)
+__device__ __forceinline__ void a_load_lds(const uint8_t *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+template <int RB, int AROWS, int STAGES>
+__global__ __launch_bounds__(256) void k_shrink_dma(LoraArgs a) {
+  // AROWS: A rows a stage holds (16, 32 or 64: the launch's largest rank
+  // rounded up), so small ranks leave LDS for more stages in flight
+  constexpr int STAGE = (RB + AROWS) * 128;       // bytes per k-tile of 64
+  constexpr int XI = RB / 8;                      // x load instructions per stage
+  constexpr int SLOTS = (XI + AROWS / 8 + 3) / 4; // most loads per wave per stage
+  constexpr int NACC = RB == 64 ? AROWS / 16 : 1; // output blocks per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + 1024];
+
+  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
+  const int item = blockIdx.x;
+  const Item it =
+      reinterpret_cast<const Item *>(a.ws + (RB == 16 ? a.L.items_g : a.L.items_s))[item];
+  const ItemRows *ix = reinterpret_cast<const ItemRows *>(a.ws + a.L.items_gx) + item;
+  if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
+  int rk[kMaxSlices];
+  item_ranks<RB == 16>(a, ix, it.adapter, rk);
+  const int q = blockIdx.y;
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSlices; ++i)
+    if (i == q) r = rk[i];
+  // <= AROWS / 16: the plan keeps ranks within max_rank, and the launch
+  // takes AROWS >= every slice's max_rank
+  const int nb = (r + 15) >> 4;
+  if (nb == 0) return;
+  const int64_t kbeg = (int64_t)blockIdx.z * a.kchunk;
+  if (kbeg >= a.k) return;
+  const int64_t kend = min(a.k, kbeg + a.kchunk);
+  const int nkt = (int)((kend - kbeg + 63) / 64);
+  const int32_t *perm = reinterpret_cast<const int32_t *>(a.ws + a.L.perm);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NI = XI + 2 * nb;            // load instructions per stage
+  const int LMAX = (NI + 3) >> 2;        // per wave, every wave the same
+
+  // Per load slot of this wave: instruction i = 4 s + wave: x rows (i < XI),
+  // A rows (i < NI) or the zero-writing pad.  Each lane's source: x as a
+  // byte offset from the chunk's x (k-tile 0), A as a row (ARow).
+  // x's extent for the loads' range check (the host keeps it below 4 GiB - 4 KiB)
+  const uint32_t xbytes = (uint32_t)(a.L.rows * a.ldx * 2);
+  uint32_t xoff[SLOTS];
+  ARow arow[SLOTS];
+  int achunk[SLOTS];
+  const SliceRef &sr = a.sl[q];
+#pragma unroll
+  for (int sl = 0; sl < SLOTS; ++sl) {
+    const int i = 4 * sl + wave;
+    xoff[sl] = 0xFFFFFFF0u;
+    arow[sl] = ARow{nullptr, nullptr, 0, 0, 0};
+    achunk[sl] = 0;
+    if (i < XI) {
+      const int P = i * 64 + lane;
+      const int row = P >> 3;
+      const int c = (P & 7) ^ (row & 7);
+      const int rr = min(row, it.nrows - 1);  // rows past the item: any valid row, dropped
+      const int m = RB == 16 ? ix->rows[rr] : perm[it.pos + rr];
+      xoff[sl] = (uint32_t)((int64_t)m * a.ldx * 2 + kbeg * 2 + c * 16);
+    } else if (i < NI) {
+      const int P = (i - XI) * 64 + lane;
+      const int j = P >> 3;
+      const int c = (P & 7) ^ (j & 7);
+      // ranks past r: a valid row of the adapter, results dropped
+      arow[sl] = make_arow(sr.ar, it.adapter, min(j, r - 1));
+      arow_resolve(arow[sl], kbeg, kend);
+      achunk[sl] = c;
+    }
+  }
+
+  auto issue = [&](int kt) {
+    uint8_t *st = smem + (kt % STAGES) * STAGE;
+    const int64_t kt0 = kbeg + (int64_t)kt * 64;
+#pragma unroll
+    for (int sl = 0; sl < SLOTS; ++sl) {
+      if (sl >= LMAX) break;
+      const int i = 4 * sl + wave;
+      if (i < XI) {
+        // chunks past kend read as zeros (out of the buffer)
+        const int c = ((((i * 64 + lane) & 7)) ^ (((i * 64 + lane) >> 3) & 7));
+        const uint32_t off = kt0 + c * 8 < kend ? xoff[sl] + (uint32_t)kt * 128u : 0xFFFFFFF0u;
+        x_load_lds(a.x, xbytes, st + i * 1024, off);
+      } else if (i < NI) {
+        // past kend: the split's first chunk of the row (finite; its x is zero)
+        int64_t kc = kt0 + achunk[sl] * 8;
+        if (kc >= kend) kc = kbeg;
+        a_load_lds(arow_ptr(arow[sl], kc), st + RB * 128 + (i - XI) * 1024);
+      } else {
+        x_load_lds(a.x, xbytes, smem + STAGES * STAGE, 0xFFFFFFF0u);
+      }
+    }
+  };
+
+  f32x4_t acc[NACC];
+#pragma unroll
+  for (int v = 0; v < NACC; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // fragment rows: 64-row items -- x block `wave`, rank blocks 0..3;
+  // 16-row items -- x block 0, rank block `wave`
+  const bool computes = RB == 64 || wave < nb;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+  const int xrow = (RB == 64 ? wave * 16 : 0) + (lane & 15);
+  const int arow0 = RB + (RB == 64 ? 0 : wave * 16) + (lane & 15);
+
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nkt) issue(s);
+  for (int kt = 0; kt < nkt; ++kt) {
+    shrink_wait_le<SLOTS * (STAGES - 2)>(LMAX * min(STAGES - 2, nkt - 1 - kt));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + STAGES - 1 < nkt) issue(kt + STAGES - 1);
+    if (computes) {
+      const uint32_t sb = lds0 + (kt % STAGES) * STAGE;
+      typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+      u32x4v xf[2], af[2][NACC];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t pc = (uint32_t)(((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16);
+        const uint32_t xa = sb + xrow * 128 + pc;
+        const uint32_t aa = sb + arow0 * 128 + pc;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(xf[ks]) : "v"(xa));
+#pragma unroll
+        for (int v = 0; v < NACC; ++v)
+          asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(af[ks][v]) : "v"(aa), "i"(v * 16 * 128));
+      }
+      // the fragments pass through the wait, so no MFMA reads them before
+      // their LDS reads have landed
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        asm volatile("" : "+v"(xf[ks]));
+#pragma unroll
+        for (int v = 0; v < NACC; ++v) asm volatile("" : "+v"(af[ks][v]));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int v = 0; v < NACC; ++v)
+          acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xf[ks]),
+                                                           __builtin_bit_cast(bf16x8_t, af[ks][v]),
+                                                           acc[v], 0, 0, 0);
+    }
+  }
+
+  if (!computes) return;
+  float *tpart = reinterpret_cast<float *>(a.ws + a.L.tpart);
+#pragma unroll
+  for (int v = 0; v < NACC; ++v) {
+    const int jb = RB == 64 ? v : wave;
+    if (jb >= nb) continue;
+    const int j = jb * 16 + (lane & 15);
+    if (j >= r) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = (RB == 64 ? wave * 16 : 0) + ((lane >> 4) << 2) + e;
+      if (row < it.nrows)
+        tpart[tpart_index(blockIdx.z, it.pos + row, q, j, a.L.rows, a.n_slices, a.L.R)] = acc[v][e];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_slice,
                               hipStream_t st) {
   const unsigned gy = per_slice ? (unsigned)a.n_slices : 1u;
+  // the LDS-staged kernel addresses x with 32-bit offsets from the chunk
+  if (per_slice && a.dtype == 1 && (uint64_t)a.L.rows * a.ldx * 2 + 4096 < (1ull << 32)) {
+    int rmax = 0;
+    for (int q = 0; q < a.n_slices; ++q) rmax = std::max(rmax, (int)a.sl[q].ar.max_rank);
+    const int arows = rmax <= 16 ? 16 : rmax <= 32 ? 32 : 64;
+    const unsigned nitems = (unsigned)(rows_per_item == 16 ? a.L.items_g_cap : a.L.items_s_cap);
+    dim3 grid(nitems, gy, (unsigned)a.ksplit);
+    // stages: ~32-64 KiB of LDS per workgroup
+    if (rows_per_item == 16) {
+      if (arows == 16) hipLaunchKernelGGL((k_shrink_dma<16, 16, LORA_SS16_16>), grid, dim3(256), 0, st, a);
+      else if (arows == 32) hipLaunchKernelGGL((k_shrink_dma<16, 32, LORA_SS16_32>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_shrink_dma<16, 64, LORA_SS16_64>), grid, dim3(256), 0, st, a);
+    } else {
+      if (arows == 16) hipLaunchKernelGGL((k_shrink_dma<64, 16, LORA_SS64_16>), grid, dim3(256), 0, st, a);
+      else if (arows == 32) hipLaunchKernelGGL((k_shrink_dma<64, 32, LORA_SS64_32>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_shrink_dma<64, 64, LORA_SS64_64>), grid, dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+  }
   // per slice: at most 4 rank blocks per workgroup (ranks <= 64)
   if (rows_per_item == 16) {
     dim3 grid((unsigned)a.L.items_g_cap, gy, (unsigned)a.ksplit);

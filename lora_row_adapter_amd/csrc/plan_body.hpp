@@ -28,29 +28,29 @@ namespace plan_detail {
 
 constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 
-// Exclusive scan of one int per thread over an NT-thread block.
-// `wsum` is LDS scratch of >= NT / 64 + 1 ints; returns the exclusive prefix
-// and writes the block total to *total (every thread sees it).
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int *total) {
+// Exclusive scan of one value per thread over an NT-thread block.
+// `wsum` is LDS scratch of >= NT / 64 + 1 values; returns the exclusive
+// prefix and writes the block total to *total (every thread sees it).
+template <int NT, typename T = int>
+__device__ __forceinline__ T block_exclusive_scan(T v, T *wsum, T *total) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  int x = v;
+  T x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
+    T y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
   __syncthreads();  // wsum may still be read by a previous scan
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int w = (lane < NT / 64) ? wsum[lane] : 0;
-    int inc = w;
+    T w = (lane < NT / 64) ? wsum[lane] : T(0);
+    T inc = w;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(inc, o, 64);
+      T y = __shfl_up(inc, o, 64);
       if (lane >= o) inc += y;
     }
     if (lane < NT / 64) wsum[lane] = inc - w;
@@ -406,7 +406,7 @@ template <int NT>
 __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSliceL *sls,
                                               uint8_t *lds) {
   constexpr int NW = NT / 64;
-  __shared__ int wsum[32];
+  __shared__ uint64_t wsum64[32];
   __shared__ int cnt[4];
 
   const int tid = threadIdx.x;
@@ -449,8 +449,10 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSlice
     const int wr = mb / RPW;
     uint64_t pending = __ballot(b >= 0);
     while (pending != 0) {
+      // the leader is uniform: a scalar read of its lane, not an LDS
+      // permute on the loop's critical path
       const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int lb = __shfl(b, leader, 64);
+      const int lb = __builtin_amdgcn_readlane(b, leader);
       const uint64_t mask = __ballot(b == lb);
       if (lane == leader) {
         const int c = __popcll(mask);
@@ -474,11 +476,16 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSlice
     ng += (h + kRowsPerGatherItem - 1) / kRowsPerGatherItem;
     ns += (h + kRowsPerSgmvItem - 1) / kRowsPerSgmvItem;
   }
-  int n_ad = 0, n_seg = 0, n_items_g = 0, n_items_s = 0;
-  int orow = block_exclusive_scan<NT>(nrow, wsum, &n_ad);
-  int oseg = block_exclusive_scan<NT>(nseg, wsum, &n_seg);
-  int og = block_exclusive_scan<NT>(ng, wsum, &n_items_g);
-  int os = block_exclusive_scan<NT>(ns, wsum, &n_items_s);
+  // the four counts as 16-bit fields of one 64-bit scan: each total is at
+  // most M <= 8192 (every segment and item holds at least one row), so no
+  // field carries into the next
+  uint64_t tot4 = 0;
+  const uint64_t ex4 = block_exclusive_scan<NT, uint64_t>(
+      (uint64_t)nrow | (uint64_t)nseg << 16 | (uint64_t)ng << 32 | (uint64_t)ns << 48, wsum64, &tot4);
+  int orow = (int)(ex4 & 0xFFFF), oseg = (int)((ex4 >> 16) & 0xFFFF);
+  int og = (int)((ex4 >> 32) & 0xFFFF), os = (int)(ex4 >> 48);
+  const int n_ad = (int)(tot4 & 0xFFFF), n_seg = (int)((tot4 >> 16) & 0xFFFF);
+  const int n_items_g = (int)((tot4 >> 32) & 0xFFFF), n_items_s = (int)(tot4 >> 48);
   for (int s = s0; s < s1; ++s) {
     const int h = hist[s];
     hist[s] = orow;  // from here on: the adapter's first sorted position
@@ -511,12 +518,16 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSlice
       }
       ++oseg;
     }
-    // first sorted position of each wave's rows of adapter s
+    // first sorted position of each wave's rows of adapter s (the counts
+    // read before the first is overwritten: no chain of LDS round trips)
+    int cw[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) cw[w] = cntw[w * S + s];
     int run = orow;
+#pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const int c = cntw[w * S + s];
       cntw[w * S + s] = run;
-      run += c;
+      run += cw[w];
     }
     orow += h;
   }
@@ -539,7 +550,7 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSlice
     uint64_t pending = __ballot(b >= 0);
     while (pending != 0) {
       const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int lb = __shfl(b, leader, 64);
+      const int lb = __builtin_amdgcn_readlane(b, leader);
       const uint64_t mask = __ballot(b == lb);
       if (b == lb) {
         const int pos = first + __popcll(mask & ((1ull << lane) - 1ull));
