@@ -177,6 +177,11 @@ struct QGemmArgs {
 hipError_t launch_gemm_q(const QGemmArgs &a, hipStream_t st);
 hipError_t launch_shrink_gather(const LoraArgs &a, hipStream_t st);
 hipError_t launch_expand_gather(const LoraArgs &a, hipStream_t st);
+// A rows per stage the LDS-staged SGMV shrink takes for this launch (per
+// slice: the largest max_rank, else the sum over slices, each rounded up to
+// 16; as 16, 32, 64 or 128), or 0 where it cannot run (fp32, x past 32-bit
+// offsets, more than 128 rows).
+int shrink_dma_rows(const LoraArgs &a, bool per_slice);
 hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_slice,
                               hipStream_t st);
 hipError_t launch_expand_sgmv(const LoraArgs &a, int rows_per_item, hipStream_t st);

@@ -16,7 +16,6 @@ namespace lora {
 
 // MFMA shrink: one workgroup per slice (more parallelism) rather than one
 // for all slices (x read once).
-constexpr bool kShrinkPerSlice = true;
 #ifndef LORA_SHRINK_WG_TARGET
 #define LORA_SHRINK_WG_TARGET 600
 #endif
@@ -558,7 +557,10 @@ lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const
     // workgroup; the gather shrink takes one per slice and 16-rank block.
     const int64_t est_items = (Mc + rpi - 1) / rpi + std::min<int64_t>(segs, 64);
     const int64_t jblk = (R + 15) / 16;
-    const bool per_slice = kShrinkPerSlice;
+    // one workgroup for every slice's rank blocks (x rows read once for all
+    // projections) where the LDS-staged shrink holds them all, else one per
+    // slice (more workgroups)
+    const bool per_slice = !(use_mfma && n_slices > 1 && shrink_dma_rows(a, false) > 0);
     const int64_t per_split = std::max<int64_t>(
         1, use_mfma ? est_items * (per_slice ? n_slices : 1)
                     : est_items * n_slices * std::min<int64_t>(jblk, 2));

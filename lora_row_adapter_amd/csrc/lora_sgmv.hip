@@ -54,6 +54,12 @@ constexpr int RMAX_MFMA = 64; // largest max_rank these kernels take
 #ifndef LORA_SS64_64
 #define LORA_SS64_64 4
 #endif
+#ifndef LORA_SS16_128
+#define LORA_SS16_128 3
+#endif
+#ifndef LORA_SS64_128
+#define LORA_SS64_128 3
+#endif
 constexpr int kExpandCols16 = 256;  // expand columns per workgroup, 16-row items (512 measured slower)
 
 __device__ __forceinline__ bf16x8_t ld16(const void *p) {
@@ -934,12 +940,16 @@ __device__ __forceinline__ void a_load_lds(const uint8_t *src, void *lds) {
 
 template <int RB, int AROWS, int STAGES>
 __global__ __launch_bounds__(256) void k_shrink_dma(LoraArgs a) {
-  // AROWS: A rows a stage holds (16, 32 or 64: the launch's largest rank
-  // rounded up), so small ranks leave LDS for more stages in flight
+  // AROWS: A rows a stage holds (16 to 128: the launch's rank blocks per
+  // workgroup, 16 rows each), so small ranks leave LDS for more stages in
+  // flight.  grid.y == n_slices: slice blockIdx.y's rank blocks; grid.y ==
+  // 1: every slice's (the x rows are read once for all projections).
   constexpr int STAGE = (RB + AROWS) * 128;       // bytes per k-tile of 64
   constexpr int XI = RB / 8;                      // x load instructions per stage
   constexpr int SLOTS = (XI + AROWS / 8 + 3) / 4; // most loads per wave per stage
-  constexpr int NACC = RB == 64 ? AROWS / 16 : 1; // output blocks per wave
+  // output blocks per wave: 64-row items -- row block `wave` x every rank
+  // block; 16-row items -- rank blocks wave, wave + 4, ...
+  constexpr int NACC = RB == 64 ? AROWS / 16 : (AROWS + 63) / 64;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + 1024];
 
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.L.hdr);
@@ -950,15 +960,20 @@ __global__ __launch_bounds__(256) void k_shrink_dma(LoraArgs a) {
   if (item >= hdr[RB == 16 ? kHdrItemsGather : kHdrItemsSgmv]) return;
   int rk[kMaxSlices];
   item_ranks<RB == 16>(a, ix, it.adapter, rk);
-  const int q = blockIdx.y;
-  int r = 0;
+  int vlo = 0, vhi = vblock_count(a, rk);
+  if (gridDim.y > 1) {
+    int nbq = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxSlices; ++i)
-    if (i == q) r = rk[i];
+    for (int q = 0; q < kMaxSlices; ++q) {
+      if (q < (int)blockIdx.y) vlo += (rk[q] + 15) >> 4;
+      if (q == (int)blockIdx.y) nbq = (rk[q] + 15) >> 4;
+    }
+    vhi = vlo + nbq;
+  }
   // <= AROWS / 16: the plan keeps ranks within max_rank, and the launch
-  // takes AROWS >= every slice's max_rank
-  const int nb = (r + 15) >> 4;
-  if (nb == 0) return;
+  // sizes AROWS for the largest ranks
+  const int nb = vhi - vlo;
+  if (nb <= 0) return;
   const int64_t kbeg = (int64_t)blockIdx.z * a.kchunk;
   if (kbeg >= a.k) return;
   const int64_t kend = min(a.k, kbeg + a.kchunk);
@@ -979,7 +994,6 @@ __global__ __launch_bounds__(256) void k_shrink_dma(LoraArgs a) {
   uint32_t xoff[SLOTS];
   ARow arow[SLOTS];
   int achunk[SLOTS];
-  const SliceRef &sr = a.sl[q];
 #pragma unroll
   for (int sl = 0; sl < SLOTS; ++sl) {
     const int i = 4 * sl + wave;
@@ -995,10 +1009,12 @@ __global__ __launch_bounds__(256) void k_shrink_dma(LoraArgs a) {
       xoff[sl] = (uint32_t)((int64_t)m * a.ldx * 2 + kbeg * 2 + c * 16);
     } else if (i < NI) {
       const int P = (i - XI) * 64 + lane;
-      const int j = P >> 3;
+      const int j = P >> 3;  // row of the stage's A region: block vlo + j / 16
       const int c = (P & 7) ^ (j & 7);
+      int slice, jb, r;
+      vblock_find(a, rk, vlo + (j >> 4), slice, jb, r);
       // ranks past r: a valid row of the adapter, results dropped
-      arow[sl] = make_arow(sr.ar, it.adapter, min(j, r - 1));
+      arow[sl] = make_arow(a.sl[slice].ar, it.adapter, min(jb * 16 + (j & 15), r - 1));
       arow_resolve(arow[sl], kbeg, kend);
       achunk[sl] = c;
     }
@@ -1030,12 +1046,11 @@ __global__ __launch_bounds__(256) void k_shrink_dma(LoraArgs a) {
   f32x4_t acc[NACC];
 #pragma unroll
   for (int v = 0; v < NACC; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // fragment rows: 64-row items -- x block `wave`, rank blocks 0..3;
-  // 16-row items -- x block 0, rank block `wave`
   const bool computes = RB == 64 || wave < nb;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
   const int xrow = (RB == 64 ? wave * 16 : 0) + (lane & 15);
   const int arow0 = RB + (RB == 64 ? 0 : wave * 16) + (lane & 15);
+  constexpr int ASTEP = RB == 64 ? 16 : 64;  // A rows between a wave's blocks
 
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nkt) issue(s);
@@ -1057,7 +1072,7 @@ __global__ __launch_bounds__(256) void k_shrink_dma(LoraArgs a) {
         asm volatile("ds_read_b128 %0, %1" : "=v"(xf[ks]) : "v"(xa));
 #pragma unroll
         for (int v = 0; v < NACC; ++v)
-          asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(af[ks][v]) : "v"(aa), "i"(v * 16 * 128));
+          asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(af[ks][v]) : "v"(aa), "i"(v * ASTEP * 128));
       }
       // the fragments pass through the wait, so no MFMA reads them before
       // their LDS reads have landed
@@ -1082,40 +1097,52 @@ __global__ __launch_bounds__(256) void k_shrink_dma(LoraArgs a) {
   float *tpart = reinterpret_cast<float *>(a.ws + a.L.tpart);
 #pragma unroll
   for (int v = 0; v < NACC; ++v) {
-    const int jb = RB == 64 ? v : wave;
-    if (jb >= nb) continue;
+    const int b = RB == 64 ? v : wave + 4 * v;  // block of the workgroup's list
+    if (b >= nb) continue;
+    int slice, jb, r;
+    vblock_find(a, rk, vlo + b, slice, jb, r);
     const int j = jb * 16 + (lane & 15);
     if (j >= r) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = (RB == 64 ? wave * 16 : 0) + ((lane >> 4) << 2) + e;
       if (row < it.nrows)
-        tpart[tpart_index(blockIdx.z, it.pos + row, q, j, a.L.rows, a.n_slices, a.L.R)] = acc[v][e];
+        tpart[tpart_index(blockIdx.z, it.pos + row, slice, j, a.L.rows, a.n_slices, a.L.R)] = acc[v][e];
     }
   }
 }
 
 }  // namespace
 
+int shrink_dma_rows(const LoraArgs &a, bool per_slice) {
+  if (a.dtype != 1 || (uint64_t)a.L.rows * a.ldx * 2 + 4096 >= (1ull << 32)) return 0;
+  int need = 0;
+  for (int q = 0; q < a.n_slices; ++q) {
+    const int r16 = (a.sl[q].ar.max_rank + 15) / 16 * 16;
+    need = per_slice ? std::max(need, r16) : need + r16;
+  }
+  return need <= 16 ? 16 : need <= 32 ? 32 : need <= 64 ? 64 : need <= 128 ? 128 : 0;
+}
+
 hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_slice,
                               hipStream_t st) {
   const unsigned gy = per_slice ? (unsigned)a.n_slices : 1u;
-  // the LDS-staged kernel addresses x with 32-bit offsets from the chunk
-  if (per_slice && a.dtype == 1 && (uint64_t)a.L.rows * a.ldx * 2 + 4096 < (1ull << 32)) {
-    int rmax = 0;
-    for (int q = 0; q < a.n_slices; ++q) rmax = std::max(rmax, (int)a.sl[q].ar.max_rank);
-    const int arows = rmax <= 16 ? 16 : rmax <= 32 ? 32 : 64;
+  // the LDS-staged kernel (x addressed with 32-bit offsets from the chunk)
+  if (const int arows = shrink_dma_rows(a, per_slice)) {
     const unsigned nitems = (unsigned)(rows_per_item == 16 ? a.L.items_g_cap : a.L.items_s_cap);
     dim3 grid(nitems, gy, (unsigned)a.ksplit);
-    // stages: ~32-64 KiB of LDS per workgroup
+    // stages: ~16-72 KiB of LDS per workgroup (fewer stages, more
+    // workgroups per CU measured faster where a workgroup streams little)
     if (rows_per_item == 16) {
       if (arows == 16) hipLaunchKernelGGL((k_shrink_dma<16, 16, LORA_SS16_16>), grid, dim3(256), 0, st, a);
       else if (arows == 32) hipLaunchKernelGGL((k_shrink_dma<16, 32, LORA_SS16_32>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_shrink_dma<16, 64, LORA_SS16_64>), grid, dim3(256), 0, st, a);
+      else if (arows == 64) hipLaunchKernelGGL((k_shrink_dma<16, 64, LORA_SS16_64>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_shrink_dma<16, 128, LORA_SS16_128>), grid, dim3(256), 0, st, a);
     } else {
       if (arows == 16) hipLaunchKernelGGL((k_shrink_dma<64, 16, LORA_SS64_16>), grid, dim3(256), 0, st, a);
       else if (arows == 32) hipLaunchKernelGGL((k_shrink_dma<64, 32, LORA_SS64_32>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_shrink_dma<64, 64, LORA_SS64_64>), grid, dim3(256), 0, st, a);
+      else if (arows == 64) hipLaunchKernelGGL((k_shrink_dma<64, 64, LORA_SS64_64>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_shrink_dma<64, 128, LORA_SS64_128>), grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();
   }
