@@ -802,12 +802,9 @@ __global__ __launch_bounds__(PC ? 64 * WM * WN + 256 : 256) void k_gemm_bf16_pip
 // (8 x 1): per k step a wave reads (M_w + N_w) fragment rows for M_w x N_w
 // outputs, so the 4 x 2 split reads 25% fewer LDS bytes per flop (measured
 // at the 70B q+v shape with the shrink folded in: 85.4 -> 82.7 us).
-#ifndef LORA_SPLIT_WN
-#define LORA_SPLIT_WN 2
-#endif
 template <int BN, bool TX, int SK>
 __global__ __launch_bounds__(768) void k_gemm_bf16_split(PipeArgs p) {
-  constexpr int WN = ((BN + (TX ? 16 : 0)) % 32 == 0) ? LORA_SPLIT_WN : 1;
+  constexpr int WN = ((BN + (TX ? 16 : 0)) % 32 == 0) ? 2 : 1;
   pipe_body<256, BN, 8 / WN, WN, 3, true, TX, SK>(p);
 }
 

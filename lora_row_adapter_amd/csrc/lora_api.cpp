@@ -16,9 +16,6 @@ namespace lora {
 
 // MFMA shrink: one workgroup per slice (more parallelism) rather than one
 // for all slices (x read once).
-#ifndef LORA_SHRINK_WG_TARGET
-#define LORA_SHRINK_WG_TARGET 600
-#endif
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -564,7 +561,7 @@ lora_status_t linear_sliced_impl(lora_dtype_t dtype, int64_t M, int64_t k, const
     const int64_t per_split = std::max<int64_t>(
         1, use_mfma ? est_items * (per_slice ? n_slices : 1)
                     : est_items * n_slices * std::min<int64_t>(jblk, 2));
-    int64_t ks = std::max<int64_t>(1, std::min<int64_t>(kMaxKSplit, (LORA_SHRINK_WG_TARGET + per_split - 1) / per_split));
+    int64_t ks = std::max<int64_t>(1, std::min<int64_t>(kMaxKSplit, (600 + per_split - 1) / per_split));
     int64_t kchunk = (k + ks - 1) / ks;
     kchunk = (kchunk + 255) / 256 * 256;
     ks = (k + kchunk - 1) / kchunk;

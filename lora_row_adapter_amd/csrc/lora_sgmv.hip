@@ -36,30 +36,11 @@ namespace lora {
 namespace {
 
 constexpr int RMAX_MFMA = 64; // largest max_rank these kernels take
-#ifndef LORA_SS16_16
-#define LORA_SS16_16 3
-#endif
-#ifndef LORA_SS16_32
-#define LORA_SS16_32 3
-#endif
-#ifndef LORA_SS16_64
-#define LORA_SS16_64 3
-#endif
-#ifndef LORA_SS64_16
-#define LORA_SS64_16 5
-#endif
-#ifndef LORA_SS64_32
-#define LORA_SS64_32 4
-#endif
-#ifndef LORA_SS64_64
-#define LORA_SS64_64 4
-#endif
-#ifndef LORA_SS16_128
-#define LORA_SS16_128 3
-#endif
-#ifndef LORA_SS64_128
-#define LORA_SS64_128 3
-#endif
+// Stages of the LDS-staged shrink per (rows per item, A rows per stage):
+// measured on MI355X, fewer stages (more workgroups per CU) where a
+// workgroup streams little
+template <int RB, int AROWS>
+constexpr int kShrinkStages = RB == 16 ? 3 : (AROWS == 16 ? 5 : AROWS == 128 ? 3 : 4);
 constexpr int kExpandCols16 = 256;  // expand columns per workgroup, 16-row items (512 measured slower)
 
 __device__ __forceinline__ bf16x8_t ld16(const void *p) {
@@ -1134,15 +1115,15 @@ hipError_t launch_shrink_sgmv(const LoraArgs &a, int rows_per_item, bool per_sli
     // stages: ~16-72 KiB of LDS per workgroup (fewer stages, more
     // workgroups per CU measured faster where a workgroup streams little)
     if (rows_per_item == 16) {
-      if (arows == 16) hipLaunchKernelGGL((k_shrink_dma<16, 16, LORA_SS16_16>), grid, dim3(256), 0, st, a);
-      else if (arows == 32) hipLaunchKernelGGL((k_shrink_dma<16, 32, LORA_SS16_32>), grid, dim3(256), 0, st, a);
-      else if (arows == 64) hipLaunchKernelGGL((k_shrink_dma<16, 64, LORA_SS16_64>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_shrink_dma<16, 128, LORA_SS16_128>), grid, dim3(256), 0, st, a);
+      if (arows == 16) hipLaunchKernelGGL((k_shrink_dma<16, 16, kShrinkStages<16, 16>>), grid, dim3(256), 0, st, a);
+      else if (arows == 32) hipLaunchKernelGGL((k_shrink_dma<16, 32, kShrinkStages<16, 32>>), grid, dim3(256), 0, st, a);
+      else if (arows == 64) hipLaunchKernelGGL((k_shrink_dma<16, 64, kShrinkStages<16, 64>>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_shrink_dma<16, 128, kShrinkStages<16, 128>>), grid, dim3(256), 0, st, a);
     } else {
-      if (arows == 16) hipLaunchKernelGGL((k_shrink_dma<64, 16, LORA_SS64_16>), grid, dim3(256), 0, st, a);
-      else if (arows == 32) hipLaunchKernelGGL((k_shrink_dma<64, 32, LORA_SS64_32>), grid, dim3(256), 0, st, a);
-      else if (arows == 64) hipLaunchKernelGGL((k_shrink_dma<64, 64, LORA_SS64_64>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_shrink_dma<64, 128, LORA_SS64_128>), grid, dim3(256), 0, st, a);
+      if (arows == 16) hipLaunchKernelGGL((k_shrink_dma<64, 16, kShrinkStages<64, 16>>), grid, dim3(256), 0, st, a);
+      else if (arows == 32) hipLaunchKernelGGL((k_shrink_dma<64, 32, kShrinkStages<64, 32>>), grid, dim3(256), 0, st, a);
+      else if (arows == 64) hipLaunchKernelGGL((k_shrink_dma<64, 64, kShrinkStages<64, 64>>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_shrink_dma<64, 128, kShrinkStages<64, 128>>), grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();
   }
