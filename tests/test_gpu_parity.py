@@ -510,3 +510,44 @@ def test_sliced_mixed_storage_and_rank_zero(oracle_mod):
         y = y.double().cpu().numpy()
         assert normwise(y[:, :96], oracle_rows(oracle_mod, w0, w0.projections[0])) <= 2e-2
         assert normwise(y[:, 96:], oracle_rows(oracle_mod, w1, w1.projections[0])) <= 2e-2
+
+
+@pytest.mark.parametrize("M,rmax", [(300, [64, 64, 64]), (300, [64, 32]), (2048, [64, 64, 64]),
+                                    (2048, [16, 32, 16, 8])],
+                         ids=["decode-3x64", "decode-64+32", "prefill-3x64", "prefill-4"])
+def test_sliced_rank_blocks_per_workgroup(oracle_mod, M, rmax):
+    """The shrink takes every slice's rank blocks in one workgroup where they
+    fit 128 A rows (64 + 32, 16 + 32 + 16 + 8) and one workgroup per slice
+    where they do not (3 x 64); decode-sized batches run 16-row items,
+    prefill-sized runs (four adapters over 2048 rows) 64-row items.  Ragged
+    k, ranks that are not multiples of 16, rank 0 in one slice; every slice
+    of every row against the oracle, with and without the separate-shrink
+    flag (no fold at these widths either way)."""
+    say("sliced rank blocks M=%d %s" % (M, rmax))
+    k = 520
+    ds = [72, 40, 56, 24][:len(rmax)]
+    S = 4 if M == 2048 else 9
+    rng = np.random.default_rng(M + len(rmax))
+    ws, devs = [], []
+    for q, (r, d) in enumerate(zip(rmax, ds)):
+        ranks = [int(v) for v in rng.integers(1, r + 1, size=S)]
+        ranks[0] = r
+        if q == 1:
+            ranks[1] = 0
+        w = wl.custom(seed=70 + q, M=M, k=k, d=d, ranks=ranks, max_rank=r)
+        if ws:
+            w.x, w.ids = ws[0].x, ws[0].ids
+        ws.append(w)
+        devs.append(DevWorkload(w, w.projections[0]))
+    W = _stacked([dv.W for dv in devs])
+    slices = [lr.Slice(d, dv.ad, dv.scales) for d, dv in zip(ds, devs)]
+    for flags in (0, lr.FLAG_SEPARATE_SHRINK):
+        y = lr.lora_linear_sliced(devs[0].x, W, slices, devs[0].ids, flags=flags)
+        torch.cuda.synchronize()
+        y = y.double().cpu().numpy()
+        lo = 0
+        for w, d in zip(ws, ds):
+            err = normwise(y[:, lo:lo + d], oracle_rows(oracle_mod, w, w.projections[0]))
+            say("  flags %d slice d=%d normwise %.3g" % (flags, d, err))
+            assert err <= 2e-2
+            lo += d
