@@ -392,16 +392,33 @@ constexpr int kPlanRowBitsMax = 13;  // sort width of the largest batch
 static_assert((1 << kPlanRowBitsMax) == kPlanMaxRows, "kPlanMaxRows rows");
 __host__ __device__ constexpr size_t plan_count_lds(int M, int S, int NT) {
   return plan_align16((size_t)M * 4) + plan_align16((size_t)S * 4) * (2 + NT / 64) +
-         plan_align16((size_t)S);
+         plan_align16((size_t)S) + plan_align16((size_t)S) * (NT / 64);
+}
+
+// Runs of equal adapters among a wave's 64 rows (b: the lane's adapter, or
+// -1): whether the lane starts a run, and the run's length (valid at its
+// first lane).  A run ends where the next lane's adapter differs.
+__device__ __forceinline__ bool plan_run(int b, int lane, int *len) {
+  const int up = __shfl_up(b, 1, 64);
+  const int dn = __shfl_down(b, 1, 64);
+  const int prev = lane == 0 ? -1 : up;
+  const int next = lane == 63 ? -1 : dn;
+  const uint64_t ends = __ballot(b >= 0 && next != b);
+  *len = (int)__builtin_ctzll(ends >> lane) + 1;  // at a run's first lane its end is at or after it
+  return b >= 0 && prev != b;
 }
 
 // Counting-sort plan.  `lds` holds plan_count_lds(M, S, NT) bytes: the
 // rows' classes, then adapters [M], a histogram [S] (then each adapter's
 // first sorted position), each adapter's first gather item [S], per-wave
-// counts [NT / 64][S] and the adapters' validity table [S] (bytes).
+// counts [NT / 64][S], the adapters' validity table [S] (bytes) and a
+// per-wave scratch table [NT / 64][S] (bytes).
 // Wave w owns the rows [w * RPW, (w + 1) * RPW): the per-wave counts give
 // each (wave, adapter) its first sorted position, and the wave then places
 // its rows in row order, so equal adapters keep row order (stable).
+// Both passes work on runs of equal adapters within 64 rows (consecutive
+// rows of one sequence share an adapter): one count and one position per
+// run instead of a ballot loop over the distinct adapters.
 template <int NT>
 __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSliceL *sls,
                                               uint8_t *lds) {
@@ -419,6 +436,7 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSlice
   int *ibase = hist + plan_align16((size_t)S * 4) / 4;
   int *cntw = ibase + plan_align16((size_t)S * 4) / 4;
   int8_t *vt = reinterpret_cast<int8_t *>(cntw + plan_align16((size_t)S * 4) / 4 * NW);
+  int8_t *dupt = vt + plan_align16((size_t)S);  // [NW][S]: a run's lane, per wave
   int32_t *hdr = reinterpret_cast<int32_t *>(a.ws + a.L.hdr);
   int32_t *perm = reinterpret_cast<int32_t *>(a.ws + a.L.perm);
   int32_t *seg_adapter = reinterpret_cast<int32_t *>(a.ws + a.L.seg_adapter);
@@ -439,27 +457,18 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSlice
 
   // 1. classify; histogram per adapter and per (wave range, adapter).  The
   //    64 rows a wave classifies at once lie in one wave range (RPW is a
-  //    multiple of 64), so each distinct adapter among them is counted with
-  //    one atomic by its lowest lane (per-row atomics on a few hot adapters
+  //    multiple of 64); each run of one adapter among them is counted with
+  //    one atomic by its first lane (per-row atomics on a few hot adapters
   //    serialized: 24 us for 8192 rows of 8 adapters)
   for (int mb = wave * 64; mb < M; mb += NT) {
     const int m = mb + lane;
     const int b = m < M ? plan_row(a, sls, sls ? binv : nullptr, m, cnt) : -1;
     if (m < M) binv[m] = b;
     const int wr = mb / RPW;
-    uint64_t pending = __ballot(b >= 0);
-    while (pending != 0) {
-      // the leader is uniform: a scalar read of its lane, not an LDS
-      // permute on the loop's critical path
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int lb = __builtin_amdgcn_readlane(b, leader);
-      const uint64_t mask = __ballot(b == lb);
-      if (lane == leader) {
-        const int c = __popcll(mask);
-        atomicAdd(&hist[lb], c);
-        atomicAdd(&cntw[wr * S + lb], c);
-      }
-      pending &= ~mask;
+    int len;
+    if (plan_run(b, lane, &len)) {
+      atomicAdd(&hist[b], len);
+      atomicAdd(&cntw[wr * S + b], len);
     }
   }
   __syncthreads();
@@ -540,13 +549,46 @@ __device__ __forceinline__ void plan_counting(const PlanArgs &a, const PlanSlice
   //    of the 64 rows waits on no LDS read; its leader lane moves the next
   //    position on, which the wave's next 64 rows read (in order).
   const int wend = min(M, (wave + 1) * RPW);
+  int8_t *dupw = dupt + (size_t)wave * plan_align16((size_t)S);
   for (int base = wave * RPW; base < wend; base += 64) {
     const int m = base + lane;
     const int b = m < wend ? binv[m] : -1;
     const int bc = b >= 0 ? b : 0;
-    const int first = cntw[wave * S + bc];
     const int start = hist[bc];
     const int item0 = ibase[bc];
+    int len;
+    const bool head = plan_run(b, lane, &len);
+    const uint64_t heads = __ballot(head);
+    if (heads == 0) continue;
+    // Two runs of one adapter among these rows (each run's first lane
+    // writes its lane number at the adapter's entry; a lane that reads back
+    // another's shares its adapter): the general loop below.  Else each run
+    // takes the next positions of its adapter at once.
+    // (volatile: the read must see the other lanes' writes, not be
+    // forwarded from this lane's own store; a wave's LDS accesses complete
+    // in order)
+    volatile int8_t *dupv = dupw;
+    if (head) dupv[b] = (int8_t)lane;
+    const bool dup = head && dupv[b] != (int8_t)lane;
+    if (__ballot(dup) == 0) {
+      int rbase = 0;
+      if (head) {
+        rbase = cntw[wave * S + b];
+        cntw[wave * S + b] = rbase + len;
+      }
+      // the lane's run starts at the highest run start at or below it
+      const uint64_t upto = heads & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
+      const int h = 63 - (int)__builtin_clzll(upto | 1ull);
+      const int hb = __shfl(rbase, h, 64);
+      if (b >= 0) {
+        const int pos = hb + (lane - h);
+        perm[pos] = m;
+        const int rel = pos - start;
+        items_gx[item0 + rel / kRowsPerGatherItem].rows[rel % kRowsPerGatherItem] = m;
+      }
+      continue;
+    }
+    const int first = cntw[wave * S + bc];
     uint64_t pending = __ballot(b >= 0);
     while (pending != 0) {
       const int leader = __ffsll((unsigned long long)pending) - 1;
