@@ -219,15 +219,19 @@ lora_status_t lora_linear(lora_dtype_t dtype, int64_t M, int64_t k, int64_t d, c
  * adapter is valid in every slice (else it is counted and gets the base).
  * lora_linear is this call with one slice.
  * Folded shrink: for bf16 with every slice's adapters in SLOTS (16-byte
- * aligned A), the MFMA path, a shape whose base GEMM runs 128 x 144 tiles
- * (sum_i d_i a multiple of 144, e.g. the q + v pair of a 70B layer at 512
- * rows) and n_slices * n_adapters * max_rank <= 32 x the GEMM's column
- * tiles, the base GEMM also computes t = x A^T for every (slice, adapter,
- * rank) and no shrink is launched: each column tile takes 16 of those
- * columns in its k loop, and where the ranks (clamped to [0, max_rank]) sum
- * past 16 x the column tiles, 16 more in a slower second pass.
- * LORA_FLAG_SEPARATE_SHRINK turns the folding off.  Results agree with the
- * separate shrink to fp32 rounding (t is summed in another order).
+ * aligned A) or in pools whose pages hold whole A rows, the MFMA path, a
+ * shape whose base GEMM runs 128 x 144 tiles (sum_i d_i a multiple of 144,
+ * e.g. the q + v pair of a 70B layer at 512 rows) or 64 x 64 tiles (decode
+ * batches, e.g. 256 rows x 4096 columns), and n_slices * n_adapters *
+ * max_rank <= 32 x the GEMM's column tiles, the base GEMM also computes
+ * t = x A^T for every (slice, adapter, rank) and no shrink is launched:
+ * each column tile takes 16 of those columns in its k loop, and where they
+ * number more than 16 x the column tiles, 16 more in a slower second pass.
+ * (128 x 144 tiles list the ranks below each adapter's rank, clamped to
+ * [0, max_rank]; 64 x 64 tiles every rank below max_rank, the columns past
+ * an adapter's rank computed and never read.)  LORA_FLAG_SEPARATE_SHRINK
+ * turns the folding off.  Results agree with the separate shrink to fp32
+ * rounding (t is summed in another order).
  */
 #define LORA_MAX_SLICES 4
 typedef struct lora_slice {

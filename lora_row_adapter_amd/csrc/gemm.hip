@@ -201,6 +201,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most min(rem, R) tiles of LOADS loads each are in flight.
+template <int LOADS, int R>
+__device__ __forceinline__ void wait_rem(int rem) {
+  if constexpr (R <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (rem >= R) wait_vmcnt<R * LOADS>();
+    else wait_rem<LOADS, R - 1>(rem);
+  }
+}
+
 // One 16-byte-per-lane load from global memory straight into LDS:
 // lane l's bytes at [base + voff, +16) land at lds + 16 * l; lanes with
 // voff + 16 > nbytes write zeros.  (Kept out of the kernel templates: the
@@ -230,15 +241,46 @@ __device__ __forceinline__ void load16_to_lds_at(const uint8_t *src, void *lds) 
 // Start of row j of adapter a's A in slice q for the folded shrink (v =
 // slice << 16 | adapter << 8 | rank), or nullptr when a pool entry cannot
 // be used (outside the pool, or a page past the table).
+// A kernel-argument value taken into a scalar register: a per-lane select
+// among such values stays a select (of loaded arguments the compiler makes
+// a load from a per-lane argument address, whose wait would also wait for
+// every tile load in flight)
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ T *uni(T *p) {
+  return reinterpret_cast<T *>((uintptr_t)uni((int64_t)(uintptr_t)p));
+}
+
+// The slice's fields are picked by a select over the argument's entries.
 __device__ __forceinline__ const uint8_t *fused_arow(const FusedT &ft, int v, int K) {
   const int q = v >> 16, a = (v >> 8) & 255, j = v & 255;
-  if (ft.page_table[q] == nullptr) return ft.A[q] + (((int64_t)a * ft.R[q] + j) * K) * 2;
+  const uint8_t *A = uni(ft.A[0]);
+  const int32_t *pt = uni(ft.page_table[0]);
+  int R = uni(ft.R[0]), sh = uni(ft.page_shift[0]);
+  int64_t mp = uni((int64_t)ft.max_pages[0]);
+  int64_t np = uni(ft.n_pages[0]);
+#pragma unroll
+  for (int s = 1; s < kMaxSlices; ++s)
+    if (q == s) {
+      A = uni(ft.A[s]);
+      pt = uni(ft.page_table[s]);
+      R = uni(ft.R[s]);
+      sh = uni(ft.page_shift[s]);
+      mp = uni((int64_t)ft.max_pages[s]);
+      np = uni(ft.n_pages[s]);
+    }
+  if (pt == nullptr) return A + (((int64_t)a * R + j) * K) * 2;
   const int64_t off = (int64_t)j * K * 2;
-  const int64_t idx = off >> ft.page_shift[q];
-  if (idx >= ft.max_pages[q]) return nullptr;
-  const int64_t page = ft.page_table[q][(int64_t)a * ft.max_pages[q] + idx];
-  if (page < 0 || page >= ft.n_pages[q]) return nullptr;
-  return ft.A[q] + (page << ft.page_shift[q]) + (off & ((int64_t(1) << ft.page_shift[q]) - 1));
+  const int64_t idx = off >> sh;
+  if (idx >= mp) return nullptr;
+  const int64_t page = pt[(int64_t)a * mp + idx];
+  if (page < 0 || page >= np) return nullptr;
+  return A + (page << sh) + (off & ((int64_t(1) << sh) - 1));
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, bool PC, bool TX, int SK>
@@ -253,13 +295,18 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
   constexpr int B_INSTR = BROWS * 8 / 256;
   constexpr int LOADS = A_INSTR + B_INSTR;
   constexpr int A_BYTES = BM * BKB;
-  constexpr int STAGE_BYTES = (BM + BROWS) * BKB;
+  // TX where the W tile has no padding rows (BN a multiple of 32): the 16 t
+  // rows follow it in the stage, loaded by the last two producers
+  constexpr bool TXW = TX && BN % 32 == 0;
+  constexpr int STAGE_BYTES = (BM + BROWS + (TXW ? 16 : 0)) * BKB;
   constexpr int FM = BM / WM / 16;
   // TX: the t block is the last 16-column block of the last wave column
-  constexpr int FN = (BN + (TX ? 16 : 0)) / WN / 16;
+  // (TXW: every wave column has one more block slot, used by the last only)
+  constexpr int FN = TXW ? BN / WN / 16 + 1 : (BN + (TX ? 16 : 0)) / WN / 16;
   constexpr int CLD = BN + 8;                            // epilogue LDS row (bf16)
-  static_assert(FM * WM * 16 == BM && FN * WN * 16 == BN + (TX ? 16 : 0), "tile split");
-  static_assert(!TX || (PC && BROWS - BN == 16), "t rows fill the W stage's padding");
+  static_assert(FM * WM * 16 == BM && (FN - (TXW ? 1 : 0)) * WN * 16 == BN + (TX && !TXW ? 16 : 0),
+                "tile split");
+  static_assert(!TX || (PC && (TXW || BROWS - BN == 16)), "t rows fill the W stage's padding");
   constexpr int ECH = (STAGES * STAGE_BYTES >= BM * CLD * 2) ? BM : BM / 2;  // epilogue rows per pass
   static_assert(STAGES * STAGE_BYTES >= ECH * CLD * 2, "epilogue fits");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
@@ -332,14 +379,89 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
   // order) and the per-lane source rows of its padding-row loads; unused
   // columns read this tile's first x row instead (their results are dropped).
   // It issues the rest of its prologue loads first, so the ranks' latency
-  // does not hold up the first tiles.
+  // does not hold up the first tiles.  Column j of pass p of column tile tn
+  // holds triple p * cap + 16 tn + j of the ordered list.
+  // TXW: producers 2 and 3 each load 8 of the t rows (one more load per
+  // tile, lanes of rows past the list masked off).  Column j of pass p of
+  // column tile tn holds entry p * cap + tn + j * tiles_n of the list
+  // (below), so that a short list spreads over every column tile.
   constexpr int TP = (BN / 8) / B_INSTR;                // that producer
-  constexpr int TE = TX ? (TP + 1) * B_INSTR - BN / 8 : 0;  // its padding-row loads per tile
-  static_assert(!TX || (TP + 1) * B_INSTR * 8 == BROWS, "padding rows within one producer");
-  const bool t_loader = TX && producer && pw == TP;
+  constexpr int TE = TX && !TXW ? (TP + 1) * B_INSTR - BN / 8 : 0;  // its padding-row loads per tile
+  static_assert(!TX || TXW || (TP + 1) * B_INSTR * 8 == BROWS, "padding rows within one producer");
+  static_assert(!TXW || NC == 4, "two of the four producers load the t rows");
+  const bool t_loader = TX && producer && (TXW ? pw >= 2 : pw == TP);
   const uint8_t *tsrc[B_INSTR];
+  const uint8_t *tw_src = nullptr;  // TXW: this lane's t-row source (k-tile 0), or none
+  bool tw_act = false;              // TXW: this producer's t load runs (uniform)
+  // the ranks of this lane's four (slice, adapter) entries and their
+  // slices' max ranks, loaded before the prologue's tile loads so that the
+  // wait for them does not also wait for those
+  int rraw[4], rmax[4];
+  auto load_ranks = [&] {
+    if constexpr (TX && !TXW) {
+      const FusedT &ft = p.ft;
+      const int nent = ft.n_slices * ft.S;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // unconditional loads at a clamped entry, masked afterwards
+        const int fc = min(lane * 4 + u, nent - 1);
+        const int qc = fc / max(ft.S, 1);
+        // the slice's pointer and max rank picked by a select over the
+        // argument's entries (a per-lane index into them is a memory load)
+        const int32_t *rk = uni(ft.ranks[0]);
+        int rm = uni(ft.R[0]);
+#pragma unroll
+        for (int q = 1; q < kMaxSlices; ++q)
+          if (qc == q) {
+            rk = uni(ft.ranks[q]);
+            rm = uni(ft.R[q]);
+          }
+        rraw[u] = rk[fc - qc * ft.S];
+        rmax[u] = rm;
+      }
+    }
+  };
+  // TXW: the ordered list runs over every slot row (slice q, adapter a,
+  // rank j < the slice's max_rank), so it is known from the arguments alone:
+  // no load stands before the t loads and no map goes through LDS; columns
+  // past an adapter's rank are computed and never read.  txw_decode(e): list
+  // entry e as slice << 16 | adapter << 8 | rank, or -1 past the end --
+  // branch-free (selects over the slices; a = floor(r / R) as
+  // (r + 1/2) * rcp(R) in fp32, exact while r < 2^16 and R <= 128: the
+  // fraction (j + 1/2) / R stays at least 1/(2R) >= 2^-8 from an integer,
+  // far above the few-ulp error of the approximate reciprocal and product)
+  int txw_total = 0;
+  if constexpr (TXW) {
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q)
+      if (q < p.ft.n_slices) txw_total += p.ft.S * p.ft.R[q];
+  }
+  auto txw_decode = [&](int e) -> int {
+    int v = -1, base = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) {
+      const int R = q < p.ft.n_slices ? p.ft.R[q] : 0;  // uniform
+      const int span = p.ft.S * R;
+      const int r = e - base;
+      const int a = (int)(((float)r + 0.5f) * __builtin_amdgcn_rcpf((float)max(R, 1)));
+      const int vq = (q << 16) | (a << 8) | (r - a * R);
+      v = (r >= 0 && r < span) ? vq : v;
+      base += span;
+    }
+    return v;
+  };
   auto build_map = [&] {
-    if constexpr (TX) {
+    if constexpr (TXW) {
+      // this producer's 8 rows (lane l: row l / 8, chunk l % 8 of the
+      // swizzled row)
+      const FusedT &ft = p.ft;
+      const int row = 8 * (pw - 2) + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7);
+      const int v = txw_decode(tn + row * p.tiles_n);
+      const uint8_t *arow = v >= 0 ? fused_arow(ft, v, p.K) : nullptr;
+      tw_src = arow ? arow + c * 16 + kbase : nullptr;
+      tw_act = __ballot(tw_src != nullptr) != 0;
+    } else if constexpr (TX) {
       const FusedT &ft = p.ft;
       const int nent = ft.n_slices * ft.S;
       int rl[4], q4[4], a4[4], loc = 0;
@@ -349,11 +471,7 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
         const int q = f / max(ft.S, 1);
         q4[u] = q;
         a4[u] = f - q * ft.S;
-        // unconditional loads at a clamped entry, masked afterwards
-        const int fc = min(f, nent - 1);
-        const int qc = fc / max(ft.S, 1);
-        const int r = min(max(ft.ranks[qc][fc - qc * ft.S], 0), ft.R[qc]);
-        rl[u] = f < nent ? r : 0;
+        rl[u] = f < nent ? min(max(rraw[u], 0), rmax[u]) : 0;
         loc += rl[u];
       }
       int inc = loc;
@@ -401,12 +519,16 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
     }
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
-      if (TX && t_loader && (pw * B_INSTR + i) * 8 >= BN) {
+      if (TX && !TXW && t_loader && (pw * B_INSTR + i) * 8 >= BN) {
         if (part != 1) load16_to_lds_at(tsrc[i] + kb, sb + (pw * B_INSTR + i) * 1024);
       } else if (part != 2) {
         load16_to_lds(wb, b_bytes, sb + (pw * B_INSTR + i) * 1024,
                       vb[i] == 0xFFFFFFF0u ? vb[i] : vb[i] + kb);
       }
+    }
+    // TXW: one load of 8 t rows, issued where any of its lanes has a row
+    if (TXW && t_loader && tw_act && part != 1) {
+      if (tw_src != nullptr) load16_to_lds_at(tw_src + kb, sb + BROWS * BKB + (pw - 2) * 1024);
     }
   };
 
@@ -416,15 +538,41 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+
   const int wm0 = (pw / WN) * (FM * 16);
-  const int wn0 = (pw % WN) * (FN * 16);
+  const int wn0 = (pw % WN) * (TXW ? BN / WN : FN * 16);
   // TX: whether this wave's last column block is the t block (uniform)
   const bool t_wave = TX && (pw % WN) == WN - 1;
 
+  // TX: the ids of the t wave's rows: one batch of loads at clamped rows,
+  // then two per register (ids outside [0, 256) -- none or invalid, never an
+  // adapter of the map -- as 0xFFFF)
+  uint32_t idr[TX ? FM : 1][4], id2[TX ? FM : 1][2];
+  auto load_ids = [&] {
+    if constexpr (TX) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          idr[i][e] = (uint32_t)p.ft.ids[min(m0 + wm0 + i * 16 + ((lane >> 4) << 2) + e, p.M - 1)];
+    }
+  };
+  auto pack_ids = [&] {
+    if constexpr (TX) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2)
+          id2[i][e >> 1] = (idr[i][e] < 256u ? idr[i][e] : 0xFFFFu) |
+                           ((idr[i][e + 1] < 256u ? idr[i][e + 1] : 0xFFFFu) << 16);
+    }
+  };
+
   // one k32 step: fragments of this wave's rows and of every column block
   // (one base offset per operand, the blocks at immediate offsets), then
-  // the FM x FN MFMAs
-  auto kstep = [&](int soff, int ks) {
+  // the FM x FN MFMAs (TXW: FN - 1 without this tile's t block)
+  auto kstep = [&](int soff, int ks, auto ton) {
+    constexpr int NJ = (TXW && !decltype(ton)::value) ? FN - 1 : FN;
     const int pc = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
     int ao = soff + (wm0 + (lane & 15)) * BKB + pc;
     int bo = soff + A_BYTES + (wn0 + (lane & 15)) * BKB + pc;
@@ -436,43 +584,53 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(smem + ao + i * 16 * BKB);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t *>(smem + bo + j * 16 * BKB);
+    for (int j = 0; j < NJ; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t *>(smem + bo + j * 16 * BKB);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
-  auto compute = [&](int kt) {
+  auto compute = [&](int kt, auto ton) {
     const int soff = (kt % STAGES) * STAGE_BYTES;
-    kstep(soff, 0);
+    kstep(soff, 0, ton);
     // with two MFMA waves per SIMD the other wave covers the fragment
     // latency; keeping this wave's k32 steps apart holds its registers to
     // one fragment set
     if constexpr (NC == 8) __builtin_amdgcn_sched_barrier(0);
-    kstep(soff, 1);
+    kstep(soff, 1, ton);
   };
-  auto wait_tile = [&](int kt) {
-    if (t_loader && kt < STAGES - 2) {
-      // its prologue issued the padding rows of tiles 0..STAGES-2 after the
+  // LT loads per tile, the last TL of them (the t rows) issued in the
+  // prologue after the others
+  auto wait_tile_t = [&](int kt, auto lt_c, auto tl_c) {
+    constexpr int LT = decltype(lt_c)::value, TL = decltype(tl_c)::value;
+    if (TL > 0 && kt < STAGES - 2) {
+      // its prologue issued the t rows of tiles 0..STAGES-2 after the
       // rest: what may still be in flight once tile kt has landed
       static_assert(!TX || STAGES == 3 || STAGES == 4, "prologue orders for 2 or 3 tiles ahead");
       if (STAGES == 3) {
-        if (nk >= 2) wait_vmcnt<TE>();
+        if (nk >= 2) wait_vmcnt<TL>();
         else wait_vmcnt<0>();
       } else if (kt == 0) {
-        if (nk >= 3) wait_vmcnt<2 * TE>();
+        if (nk >= 3) wait_vmcnt<2 * TL>();
         else wait_vmcnt<0>();
       } else {
-        if (nk >= 4) wait_vmcnt<TE + LOADS>();
+        if (nk >= 4) wait_vmcnt<TL + LT>();
         else wait_vmcnt<0>();
       }
       return;
     }
-    const int rem = min(STAGES - 2, nk - 1 - kt);
-    if (rem >= 2) wait_vmcnt<2 * LOADS>();
-    else if (rem == 1) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
+    // the tiles after kt that may stay in flight: up to STAGES - 2
+    wait_rem<LT, (STAGES - 2 < 63 / LT ? STAGES - 2 : 63 / LT)>(min(STAGES - 2, nk - 1 - kt));
+  };
+  auto wait_tile = [&](int kt) {
+    using I0 = std::integral_constant<int, 0>;
+    if (TXW && t_loader && tw_act)
+      wait_tile_t(kt, std::integral_constant<int, LOADS + 1>{}, I0{});
+    else if (TX && !TXW && t_loader)
+      wait_tile_t(kt, std::integral_constant<int, LOADS>{}, std::integral_constant<int, TE>{});
+    else
+      wait_tile_t(kt, std::integral_constant<int, LOADS>{}, I0{});
   };
   // Raw barriers below: a wave's loads of tile kt are complete (vmcnt);
   // after the barrier every loading wave's are, and every multiplying wave
@@ -485,7 +643,15 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
     asm volatile("" ::: "memory");
   };
 
-  if (t_loader) {
+  if (TXW && t_loader) {
+    // the t rows' sources first, while no load is in flight (arithmetic on
+    // the arguments), then the tiles with their t rows in order
+    build_map();
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(s, s);
+  } else if (t_loader) {
+    load_ranks();
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < nk) issue(s, s, 1);
@@ -498,69 +664,81 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < nk) issue(s, s);
   }
+  // Explicit LDS fragment reads, for the waves whose fragment latency
+  // nothing else covers (one MFMA wave per SIMD): ds_read_b128 with explicit
+  // lgkmcnt waits.  As ordinary loads the compiler cannot tell them from the
+  // stages the DMA is still filling and waits for every load in flight
+  // before each read.  NJ: the column blocks read and multiplied.
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+  auto lfrag = [&](int soff, int ks, u32x4v (&af)[FM], u32x4v (&bfr)[FN], auto njc) {
+    constexpr int NJ = decltype(njc)::value;
+    const int pc = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+    const uint32_t ao = lds0 + soff + (wm0 + (lane & 15)) * BKB + pc;
+    const uint32_t bo = lds0 + soff + A_BYTES + (wn0 + (lane & 15)) * BKB + pc;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(af[i]) : "v"(ao), "i"(i * 16 * BKB));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(bfr[j]) : "v"(bo), "i"(j * 16 * BKB));
+  };
+  // at most N LDS reads outstanding; the fragments pass through the
+  // statements, so nothing reads them before the wait
+  auto fwait = [&](auto nconst, u32x4v (&af)[FM], u32x4v (&bfr)[FN], auto njc) {
+    constexpr int N = decltype(nconst)::value, NJ = decltype(njc)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(af[i]));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(bfr[j]));
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+#pragma unroll
+    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(af[i]));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(bfr[j]));
+  };
+  auto mma = [&](const u32x4v (&af)[FM], const u32x4v (&bfr)[FN], auto njc) {
+    constexpr int NJ = decltype(njc)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
+                                                            __builtin_bit_cast(bf16x8_t, bfr[j]),
+                                                            acc[i][j], 0, 0, 0);
+  };
+  // the four MFMA waves of the folded 64 x 64 tiles double-buffer their
+  // fragments (measured at 256 x 4096 x 4096: 19.3 -> 18.5 us folded; the
+  // plain tiles gain nothing)
+  constexpr bool DB = PC && NC == 4 && TXW;
+  static_assert(!TXW || (BM == 64 && BN == 64), "the t rows past the W tile: 64 x 64 tiles");
+  using FNc = std::integral_constant<int, FN>;
+
   if constexpr (!PC) {
     // One MFMA wave per SIMD that also issues its share of the tile loads
     // (256 x 256 tiles: the accumulators take a SIMD's registers).  Nothing
     // else hides the fragment reads, so they are double-buffered: k-step
     // 1's fragments load during k-step 0's MFMAs, the next tile's k-step 0
     // fragments during k-step 1's (its barrier comes between the two, once
-    // this tile's reads have landed).  The reads are explicit ds_read_b128
-    // with explicit lgkmcnt waits: as ordinary loads the compiler cannot tell
-    // them from the stages the DMA is still filling and waits for every load
-    // in flight before each read (then each read's latency was exposed:
-    // 43% MFMA busy at the 8192 x 4096 x 4096 prefill shape).
-    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    // this tile's reads have landed).  (As ordinary loads each read's
+    // latency was exposed: 43% MFMA busy at the 8192 x 4096 x 4096 prefill
+    // shape.)
     u32x4v fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
-    auto lfrag = [&](int soff, int ks, u32x4v (&af)[FM], u32x4v (&bfr)[FN]) {
-      const int pc = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
-      const uint32_t ao = lds0 + soff + (wm0 + (lane & 15)) * BKB + pc;
-      const uint32_t bo = lds0 + soff + A_BYTES + (wn0 + (lane & 15)) * BKB + pc;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(af[i]) : "v"(ao), "i"(i * 16 * BKB));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(bfr[j]) : "v"(bo), "i"(j * 16 * BKB));
-    };
-    // at most N LDS reads outstanding; the fragments pass through the
-    // statements, so nothing reads them before the wait
-    auto fwait = [&](auto nconst, u32x4v (&af)[FM], u32x4v (&bfr)[FN]) {
-      constexpr int N = decltype(nconst)::value;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(af[i]));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(bfr[j]));
-      asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
-#pragma unroll
-      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(af[i]));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(bfr[j]));
-    };
     // the waits count LDS reads in order: once at most FM + FN of the
     // later set are outstanding (15 at most, the counter's range), the
     // earlier set has landed
     constexpr int NFR = FM + FN < 15 ? FM + FN : 15;
-    auto mma = [&](const u32x4v (&af)[FM], const u32x4v (&bfr)[FN]) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
-                                                              __builtin_bit_cast(bf16x8_t, bfr[j]),
-                                                              acc[i][j], 0, 0, 0);
-    };
     wait_tile(0);
     barrier();
     if (STAGES - 1 < nk) issue(STAGES - 1, (STAGES - 1) % STAGES);
-    lfrag(0, 0, fa0, fb0);
+    lfrag(0, 0, fa0, fb0, FNc{});
     // the last tile is peeled off so that the loop body has no branch
     // around the next tile's reads (the compiler would merge the wait counts
     // of both paths and wait for those reads too)
     for (int kt = 0; kt < nk - 1; ++kt) {
-      lfrag((kt % STAGES) * STAGE_BYTES, 1, fa1, fb1);
-      fwait(std::integral_constant<int, NFR>{}, fa0, fb0);
-      mma(fa0, fb0);
+      lfrag((kt % STAGES) * STAGE_BYTES, 1, fa1, fb1, FNc{});
+      fwait(std::integral_constant<int, NFR>{}, fa0, fb0, FNc{});
+      mma(fa0, fb0, FNc{});
       // the k-step-0 MFMAs stay ahead of the wait for the next tile's loads
       // (the scheduler would otherwise sink them past the barrier and the
       // wait would no longer overlap them)
@@ -568,28 +746,65 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       wait_tile(kt + 1);
       // this wave's reads of tile kt are in registers before the barrier
       // that lets tile kt + STAGES overwrite its stage
-      fwait(std::integral_constant<int, 0>{}, fa1, fb1);
+      fwait(std::integral_constant<int, 0>{}, fa1, fb1, FNc{});
       barrier();
       if (kt + STAGES < nk) issue(kt + STAGES, (kt + STAGES) % STAGES);
-      lfrag(((kt + 1) % STAGES) * STAGE_BYTES, 0, fa0, fb0);
-      mma(fa1, fb1);
+      lfrag(((kt + 1) % STAGES) * STAGE_BYTES, 0, fa0, fb0, FNc{});
+      mma(fa1, fb1, FNc{});
       __builtin_amdgcn_sched_barrier(0);
     }
-    lfrag(((nk - 1) % STAGES) * STAGE_BYTES, 1, fa1, fb1);
-    fwait(std::integral_constant<int, NFR>{}, fa0, fb0);
-    mma(fa0, fb0);
-    fwait(std::integral_constant<int, 0>{}, fa1, fb1);
-    mma(fa1, fb1);
+    lfrag(((nk - 1) % STAGES) * STAGE_BYTES, 1, fa1, fb1, FNc{});
+    fwait(std::integral_constant<int, NFR>{}, fa0, fb0, FNc{});
+    mma(fa0, fb0, FNc{});
+    fwait(std::integral_constant<int, 0>{}, fa1, fb1, FNc{});
+    mma(fa1, fb1, FNc{});
   } else if (producer) {
     for (int kt = 0; kt < nk; ++kt) {
       wait_tile(kt);
       barrier();
       if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
     }
+  } else if constexpr (DB) {
+    // Four MFMA waves, one per SIMD (the folded 64 x 64 tiles): as for the
+    // single-role waves above, k-step 1's fragments load during k-step 0's
+    // MFMAs and the next tile's k-step 0 fragments during k-step 1's, right
+    // after the barrier that releases that tile; this tile's reads have
+    // landed before the barrier after which its stage is refilled.
+    // TXW: the t block only in the last wave column, and only where this
+    // tile has a triple.
+    barrier();
+    const bool ton = !TXW || (t_wave && txw_total > tn);
+    auto loop = [&](auto njc) {
+      constexpr int NJ = decltype(njc)::value;
+      constexpr int NFR = FM + NJ < 15 ? FM + NJ : 15;
+      using NFc = std::integral_constant<int, NFR>;
+      using Z = std::integral_constant<int, 0>;
+      u32x4v fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+      lfrag(0, 0, fa0, fb0, njc);
+      for (int kt = 0; kt < nk - 1; ++kt) {
+        const int soff = (kt % STAGES) * STAGE_BYTES;
+        lfrag(soff, 1, fa1, fb1, njc);
+        fwait(NFc{}, fa0, fb0, njc);
+        mma(fa0, fb0, njc);
+        __builtin_amdgcn_sched_barrier(0);
+        fwait(Z{}, fa1, fb1, njc);
+        barrier();
+        lfrag(((kt + 1) % STAGES) * STAGE_BYTES, 0, fa0, fb0, njc);
+        mma(fa1, fb1, njc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lfrag(((nk - 1) % STAGES) * STAGE_BYTES, 1, fa1, fb1, njc);
+      fwait(NFc{}, fa0, fb0, njc);
+      mma(fa0, fb0, njc);
+      fwait(Z{}, fa1, fb1, njc);
+      mma(fa1, fb1, njc);
+    };
+    if (!TXW || ton) loop(FNc{});
+    else loop(std::integral_constant<int, TXW ? FN - 1 : FN>{});
   } else {
     for (int kt = 0; kt < nk; ++kt) {
       barrier();
-      compute(kt);
+      compute(kt, std::true_type{});
     }
   }
 
@@ -682,22 +897,12 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
 
   if constexpr (TX) {
     // t: this tile's rows x its 16 t columns, kept where the row's adapter
-    // owns the column (tmap was written before the k loop's barriers)
+    // owns the column (tmap was written before the k loop's barriers;
+    // TXW: the list decoded from the arguments)
     if (owner && t_wave) {
       const FusedT &ft = p.ft;
-      // the rows' ids first (one batch of loads at clamped rows)
-      // (two per register: ids outside [0, 256) -- none or invalid, never
-      // an adapter of the map -- as 0xFFFF)
-      uint32_t id2[FM][2];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const int r = m0 + wm0 + i * 16 + ((lane >> 4) << 2) + e;
-          const uint32_t lo = (uint32_t)ft.ids[min(r, p.M - 1)];
-          const uint32_t hi = (uint32_t)ft.ids[min(r + 1, p.M - 1)];
-          id2[i][e >> 1] = (lo < 256u ? lo : 0xFFFFu) | ((hi < 256u ? hi : 0xFFFFu) << 16);
-        }
+      load_ids();
+      pack_ids();
       auto scatter = [&](int v, const f32x4_t (&t)[FM]) {
         if (v < 0) return;
         const int q = v >> 16, a = (v >> 8) & 255, j = v & 255;
@@ -713,12 +918,12 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       f32x4_t t0[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i) t0[i] = tile_val(i, FN - 1);
-      scatter(tmap[lane & 15], t0);
-      if (tmap[32] > ft.cap) {  // uniform
+      scatter(TXW ? txw_decode(tn + (lane & 15) * p.tiles_n) : tmap[lane & 15], t0);
+      if ((TXW ? txw_total : tmap[32]) > ft.cap) {  // uniform
         // second pass: MFMA operands straight from global memory (x rows in
         // the A-operand layout, the column's A row in the B-operand layout),
         // loads at clamped rows / a valid dummy row, all issued before use
-        const int v1 = tmap[16 + (lane & 15)];
+        const int v1 = TXW ? txw_decode(ft.cap + tn + (lane & 15) * p.tiles_n) : tmap[16 + (lane & 15)];
         const int kl = (lane >> 4) * 8;
         const uint8_t *arow = v1 >= 0 ? fused_arow(ft, v1, p.K) : nullptr;
         const uint16_t *asrc = arow ? reinterpret_cast<const uint16_t *>(arow) + kl
@@ -756,7 +961,7 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       if (!owner || rb < r0 || rb >= r0 + ECH) continue;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        if (TX && j == FN - 1 && t_wave) continue;
+        if (TX && j == FN - 1 && (TXW || t_wave)) continue;
         const f32x4_t v = tile_val(i, j);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -913,6 +1118,10 @@ bool pipe_ok(int64_t k, int64_t ldx, int64_t ldw) {
          (uint64_t)256 * ldw * 2 < (1ull << 32);
 }
 
+// LDS stages of the 64 x 64 tiles (measured at 256 x 4096 x 4096: 3
+// stages 18.3 us, 4 15.4, 6 21.7, 8 19.6)
+constexpr int kStages64 = 4;
+
 // Tile choice: fill the 256 CUs with as few, as large tiles as possible.
 // Relative per-FLOP costs of the shapes were measured on MI355X (bigger
 // tiles move fewer bytes per FLOP into LDS).  Returns the index into the
@@ -1043,7 +1252,7 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
           break;
         case 3: ok = launch_pipe<128, 128, 2, 2, 4>(pa, st, plan); break;
         case 5: ok = launch_wide(pa, M, d, st, plan); break;
-        default: ok = launch_pipe<64, 64, 2, 2, 4>(pa, st, plan); break;
+        default: ok = launch_pipe<64, 64, 2, 2, kStages64>(pa, st, plan); break;
       }
       return ok ? hipGetLastError() : hipErrorInvalidValue;
     }
@@ -1062,8 +1271,11 @@ hipError_t launch_gemm(int32_t dtype, int64_t M, int64_t k, int64_t d, const voi
 }
 
 int32_t gemm_fused_cap(int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw) {
-  if (M <= 0 || d <= 0 || !pipe_ok(k, ldx, ldw) || choose_tile(M, d) != 2) return 0;
-  return (int32_t)(16 * ((d + 143) / 144));
+  if (M <= 0 || d <= 0 || !pipe_ok(k, ldx, ldw)) return 0;
+  const int tile = choose_tile(M, d);
+  if (tile == 2) return (int32_t)(16 * ((d + 143) / 144));
+  if (tile == 4) return (int32_t)(16 * ((d + 63) / 64));
+  return 0;
 }
 
 // The kernel and block size launch_gemm / launch_gemm_fused would run.
@@ -1078,7 +1290,8 @@ static void gemm_pick(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ld
     *fn = (const void *)k_gemm_bf16;
     return;
   }
-  switch (fused ? 2 : choose_tile(M, d)) {
+  const int tile = choose_tile(M, d);
+  switch (fused && tile != 4 ? 2 : tile) {
     case 0: *fn = (const void *)k_gemm_bf16_pipe<256, 256, 2, 2, 2, false, false>; break;
     case 1: *fn = (const void *)k_gemm_bf16_pipe<256, 128, 4, 1, 3, true, false>; *threads = 512; break;
     case 2:
@@ -1094,7 +1307,11 @@ static void gemm_pick(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ld
       break;
     case 3: *fn = (const void *)k_gemm_bf16_pipe<128, 128, 2, 2, 4, true, false>; *threads = 512; break;
     case 5: *fn = (const void *)k_gemm_bf16_split<160, false, 1>; *threads = 768; break;
-    default: *fn = (const void *)k_gemm_bf16_pipe<64, 64, 2, 2, 4, true, false>; *threads = 512; break;
+    default:
+      *fn = fused ? (const void *)k_gemm_bf16_pipe<64, 64, 2, 2, kStages64, true, true>
+                  : (const void *)k_gemm_bf16_pipe<64, 64, 2, 2, kStages64, true, false>;
+      *threads = 512;
+      break;
   }
 }
 
@@ -1121,7 +1338,9 @@ hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int
     return hipErrorInvalidValue;
   PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
   pa.ft = ft;
-  if (split_ok(M, k, d, gws, gws_bytes)) {
+  if (choose_tile(M, d) == 4) {
+    if (!launch_pipe<64, 64, 2, 2, kStages64, true>(pa, st, plan)) return hipErrorInvalidValue;
+  } else if (split_ok(M, k, d, gws, gws_bytes)) {
     launch_split<true>(pa, M, d, gws, expired, st, plan);
   } else if (!launch_pipe<128, 144, 4, 1, 3, true>(pa, st, plan)) {
     return hipErrorInvalidValue;
@@ -1132,7 +1351,7 @@ hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int
 bool gemm_runs_plan(int32_t dtype, int64_t M, int64_t k, int64_t d, int64_t ldx, int64_t ldw,
                     void *gws, size_t gws_bytes, bool fused) {
   if (dtype != 1 || M <= 0 || d <= 0 || !pipe_ok(k, ldx, ldw)) return false;
-  if (split_ok(M, k, d, gws, gws_bytes) && (fused || choose_tile(M, d) == 2)) return true;
+  if (split_ok(M, k, d, gws, gws_bytes) && choose_tile(M, d) == 2) return true;
   KernelFootprint f;
   return gemm_footprint(dtype, M, k, d, ldx, ldw, gws, gws_bytes, fused, &f) && f.lds > 0 &&
          fits_beside(f, f) && (fused || choose_tile(M, d) != 5);

@@ -1,15 +1,17 @@
 """The shrink folded into the base GEMM, on the GPU, through the C ABI.
 
-Where the base GEMM runs 128 x 144 tiles (bf16, adapters in slots), each
-column tile also computes 16 columns of t = x A^T over the stacked
-(slice, adapter, rank) list -- and 16 more in a second pass where the ranks
-sum past the first pass's capacity -- and no shrink is launched.  Checked
-against the fp64 oracle (normwise 2e-2, the layer's bf16 bound), against the
-same call with LORA_FLAG_SEPARATE_SHRINK (t summed in another order: the two
-outputs differ by bf16 rounding of y only), and through the library's own
-launch counters (which kernels ran).  Shapes: 400 rows (three full 128-row
-tiles and a 16-row tail) and sum d = 9216, the range where 128 x 144 tiles
-are chosen; k = 512 keeps the oracle fast.
+Where the base GEMM runs 128 x 144 or 64 x 64 tiles (bf16, adapters in
+slots or in pages that hold whole A rows), each column tile also computes 16
+columns of t = x A^T over the stacked (slice, adapter, rank) list -- and 16
+more in a second pass where the list is longer than the first pass's
+capacity -- and no shrink is launched.  Checked against the fp64 oracle
+(normwise 2e-2, the layer's bf16 bound), against the same call with
+LORA_FLAG_SEPARATE_SHRINK (t summed in another order: the two outputs differ
+by bf16 rounding of y only), and through the library's own launch counters
+(which kernels ran).  Shapes: 400 rows (three full 128-row tiles and a
+16-row tail) and sum d = 9216, the range where 128 x 144 tiles are chosen;
+decode sizes (64 to 256 rows, ragged columns) for the 64 x 64 tiles; k <= 512
+keeps the oracle fast (the decode-4096 workload on sampled rows).
 """
 import numpy as np
 import pytest
@@ -225,3 +227,106 @@ def test_fused_pool_bad_page_entry_reads_no_adapter():
     torch.cuda.synchronize()
     rows = torch.from_numpy(np.flatnonzero(w.ids == bad)).cuda()
     assert torch.equal(y[rows], base[rows])
+
+
+# ---------------------------------------------------------------------------
+# The fold at decode sizes: 64 x 64 tiles.  Each column tile carries 16 t
+# columns past its 64 W rows; column j of column tile tn is entry
+# tn + j * tiles (then cap + tn + j * tiles for the second pass) of the list
+# of every slot row (slice, adapter, rank < the slice's max_rank), so the
+# columns past an adapter's rank are computed too and must never be read.
+# ---------------------------------------------------------------------------
+
+def check_fused_one(oracle_mod, w, pad, expect_shrink=0):
+    p = w.projections[0]
+    dw = DevWorkload(w, p, pad_value=pad)
+    res = {}
+    cnt = launches(lambda: res.setdefault("y", dw.run()))
+    assert cnt["gemm"] == 1 and cnt["sgmv_expand"] == 1, cnt
+    assert cnt["sgmv_shrink"] == expect_shrink, cnt
+    y = res["y"]
+    err = normwise(y.double().cpu().numpy(), oracle_rows(oracle_mod, w, p))
+    say("  normwise %.3g" % err)
+    assert err <= 2e-2
+    ysep = dw.run(flags=lr.FLAG_SEPARATE_SHRINK)
+    assert normwise(y.double().cpu().numpy(), ysep.double().cpu().numpy()) <= 1e-2
+    base = lr.lora_gemm(dw.x, dw.W)
+    torch.cuda.synchronize()
+    none = torch.from_numpy(np.flatnonzero(w.ids < 0)).cuda()
+    assert torch.equal(y[none], base[none])
+    return dw, y
+
+
+@pytest.mark.parametrize("M,k,d,ranks,R", [
+    (200, 320, 1000, [16, 8, 0, 13, 16, 4], 16),   # ragged rows and columns, one pass
+    (150, 128, 128, [16, 16, 16], 16),             # 48 entries past the 32-column first pass
+    (64, 320, 64, [8, 3], 8),                      # one tile, the first pass exactly full
+])
+@pytest.mark.parametrize("pad", [0.0, float("nan")])
+def test_decode_tiles_fused(oracle_mod, M, k, d, ranks, R, pad):
+    """bf16 slots at shapes run as 64 x 64 tiles: no shrink launched; every
+    row against the oracle; within bf16 rounding of the separate shrink;
+    rows without an adapter bitwise the base GEMM.  pad = NaN fills the
+    slots past each adapter's rank (A rows and B columns), which the fold
+    multiplies into t columns that the expand must not read."""
+    w = wl.custom(seed=40 + M + d, M=M, k=k, d=d, ranks=ranks, max_rank=R, none_frac=0.1)
+    say("decode tiles fused: M=%d k=%d d=%d ranks=%s pad=%s" % (M, k, d, ranks, pad))
+    check_fused_one(oracle_mod, w, pad)
+
+
+def test_decode_tiles_fused_c1(oracle_mod):
+    """The decode-4096 workload (256 rows, 4 slots of rank 16) on its
+    benchmarked path: the shrink folded into the 64 x 64 GEMM; sampled rows
+    of every adapter against the oracle."""
+    w = wl.c1_decode_bf16()
+    p = w.projections[0]
+    dw = DevWorkload(w, p)
+    res = {}
+    cnt = launches(lambda: res.setdefault("y", dw.run()))
+    assert cnt["gemm"] == 1 and cnt["sgmv_shrink"] == 0 and cnt["sgmv_expand"] == 1, cnt
+    rows = np.concatenate([np.flatnonzero(w.ids == a)[:6] for a in range(-1, w.S)])
+    ref = oracle_rows(oracle_mod, w, p, rows=rows)
+    err = normwise(res["y"][torch.from_numpy(rows).cuda()].double().cpu().numpy(), ref)
+    say("c1 fused sampled normwise %.3g" % err)
+    assert err <= 2e-2
+
+
+def test_decode_tiles_two_slices_two_passes(oracle_mod):
+    """q + v slices with the 70B adapter set at 128 rows and sum d = 3072:
+    48 column tiles, a 768-column first pass, 1536 slot rows -- the second
+    pass carries half of them.  Slots, then the same adapters in 4 KiB
+    pages (bitwise the same output)."""
+    w = wl.c3_proj70b_bf16(M=128, k=256, d_q=2560, d_v=512)
+    W, slices, _keep = sliced_pair(w)
+    x, ids = w.x.cuda(), torch.from_numpy(w.ids).cuda()
+    res = {}
+    cnt = launches(lambda: res.setdefault("y", lr.lora_linear_sliced(x, W, slices, ids)))
+    assert cnt["gemm"] == 1 and cnt["sgmv_shrink"] == 0 and cnt["sgmv_expand"] == 1, cnt
+    y = res["y"]
+    for p, lo in ((w.proj("q"), 0), (w.proj("v"), 2560)):
+        err = normwise(y[:, lo:lo + p.d].double().cpu().numpy(), oracle_rows(oracle_mod, w, p))
+        say("  %s normwise %.3g" % (p.name, err))
+        assert err <= 2e-2
+    Wp, pslices, _kp = pooled_pair(w, 4096)
+    yp = lr.lora_linear_sliced(x, Wp, pslices, ids)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yp)
+
+
+def test_decode_tiles_out_of_range_ranks(oracle_mod):
+    """Ranks above max_rank or below zero at 64 x 64 tiles: the fold's list
+    does not depend on them; the plan turns those adapters' rows into base
+    rows."""
+    w = wl.custom(seed=47, M=200, k=320, d=1000, ranks=[16, 16, 8, 4], max_rank=16)
+    p = w.projections[0]
+    dw = DevWorkload(w, p)
+    dw.ranks[1] = 1000
+    dw.ranks[2] = -3
+    y = dw.run()
+    ids = w.ids.copy()
+    ids[np.isin(ids, [1, 2])] = -1
+    err = normwise(y.double().cpu().numpy(), oracle_rows(oracle_mod, w, p, ids=ids))
+    assert err <= 2e-2
+    base = lr.lora_gemm(dw.x, dw.W)
+    bad = torch.from_numpy(np.flatnonzero(np.isin(w.ids, [1, 2]))).cuda()
+    assert torch.equal(y[bad], base[bad])
