@@ -223,6 +223,11 @@ def main():
            for kname in lr.KERNEL_CLASSES}
     launches = {kname: prof[kname]["launches"] for kname in lr.KERNEL_CLASSES}
     log("per-launch us: " + json.dumps({k_: round(v, 2) for k_, v in per.items()}))
+    # the same steps reusing the plan already in the workspace (same ids): the
+    # base GEMM launch without the plan it otherwise carries
+    rprof, _ = profiled(prof_steps, lr.FLAG_REUSE_PLAN)
+    gemm_us_reused = rprof["gemm"]["ms"] * 1e3 / max(rprof["gemm"]["launches"], 1)
+    log("gemm us with the plan reused: %.2f" % gemm_us_reused)
 
     # per-step GPU time from events between steps on the stream (rotating
     # buffer sets, as timed), and the same with one buffer set only (warm:
@@ -336,6 +341,8 @@ def main():
             "event_pass_ms_per_step": round(ev_elapsed * 1e3 / prof_steps, 4),
             "tokens_per_s_from_kernel_sum": M / (kernel_us_step * 1e-6),
             "gemm_tflops": round(gemm_tflops, 1),
+            "gemm_us_plan_reused": round(gemm_us_reused, 2),
+            "plan_in_gemm_us": round(per["gemm"] - gemm_us_reused, 2),
             "shrink_folded_into_gemm": folded,
             "shrink_gbs": round(shrink_gbs, 1),
             "shrink_frac_hbm": round(shrink_gbs / HBM_PEAK_GBS, 4),

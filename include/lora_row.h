@@ -108,8 +108,8 @@ typedef enum lora_adapter_kind {
  * SLOTS: A [n_adapters, max_rank, k] and B [n_adapters, d, max_rank], same
  *   dtype as x.  Slot s holds A_s in rows 0..r_s-1 of A[s] and B_s in columns
  *   0..r_s-1 of B[s]; padding may hold anything (NaN included) and never
- *   reaches the result (a kernel may load it inside a 16-byte vector, but
- *   zeroes it first).
+ *   reaches the result (a kernel may load it, inside a 16-byte vector that
+ *   it zeroes first, or as whole rows of A whose products it never reads).
  * POOL: `pool` is n_pages * page_bytes bytes.  Adapter a's logical byte space
  *   is A_a (r_a x k, row-major) followed by B_a (d x r_a, row-major, row
  *   stride r_a), both unpadded, in x's dtype; logical page j of it is physical
