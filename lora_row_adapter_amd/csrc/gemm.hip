@@ -382,9 +382,11 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
   // does not hold up the first tiles.  Column j of pass p of column tile tn
   // holds triple p * cap + 16 tn + j of the ordered list.
   // TXW: producers 2 and 3 each load 8 of the t rows (one more load per
-  // tile, lanes of rows past the list masked off).  Column j of pass p of
-  // column tile tn holds entry p * cap + tn + j * tiles_n of the list
-  // (below), so that a short list spreads over every column tile.
+  // tile, lanes of rows past the list masked off), column j of pass p of
+  // column tile tn again holding entry p * cap + 16 tn + j of the list
+  // (below); the column tiles past the list skip the t block.  (Spreading
+  // a short list over every column tile, entry tn + j * tiles_n, measured
+  // 0.45 us slower at 256 x 4096 x 4096: every tile then pays the block.)
   constexpr int TP = (BN / 8) / B_INSTR;                // that producer
   constexpr int TE = TX && !TXW ? (TP + 1) * B_INSTR - BN / 8 : 0;  // its padding-row loads per tile
   static_assert(!TX || TXW || (TP + 1) * B_INSTR * 8 == BROWS, "padding rows within one producer");
@@ -457,7 +459,7 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       const FusedT &ft = p.ft;
       const int row = 8 * (pw - 2) + (lane >> 3);
       const int c = (lane & 7) ^ (row & 7);
-      const int v = txw_decode(tn + row * p.tiles_n);
+      const int v = txw_decode(16 * tn + row);
       const uint8_t *arow = v >= 0 ? fused_arow(ft, v, p.K) : nullptr;
       tw_src = arow ? arow + c * 16 + kbase : nullptr;
       tw_act = __ballot(tw_src != nullptr) != 0;
@@ -771,9 +773,9 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
     // after the barrier that releases that tile; this tile's reads have
     // landed before the barrier after which its stage is refilled.
     // TXW: the t block only in the last wave column, and only where this
-    // tile has a triple.
+    // tile has a list entry.
     barrier();
-    const bool ton = !TXW || (t_wave && txw_total > tn);
+    const bool ton = !TXW || (t_wave && txw_total > 16 * tn);
     auto loop = [&](auto njc) {
       constexpr int NJ = decltype(njc)::value;
       constexpr int NFR = FM + NJ < 15 ? FM + NJ : 15;
@@ -918,12 +920,12 @@ __device__ __forceinline__ void pipe_body(const PipeArgs &p) {
       f32x4_t t0[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i) t0[i] = tile_val(i, FN - 1);
-      scatter(TXW ? txw_decode(tn + (lane & 15) * p.tiles_n) : tmap[lane & 15], t0);
+      scatter(TXW ? txw_decode(16 * tn + (lane & 15)) : tmap[lane & 15], t0);
       if ((TXW ? txw_total : tmap[32]) > ft.cap) {  // uniform
         // second pass: MFMA operands straight from global memory (x rows in
         // the A-operand layout, the column's A row in the B-operand layout),
         // loads at clamped rows / a valid dummy row, all issued before use
-        const int v1 = TXW ? txw_decode(ft.cap + tn + (lane & 15) * p.tiles_n) : tmap[16 + (lane & 15)];
+        const int v1 = TXW ? txw_decode(ft.cap + 16 * tn + (lane & 15)) : tmap[16 + (lane & 15)];
         const int kl = (lane >> 4) * 8;
         const uint8_t *arow = v1 >= 0 ? fused_arow(ft, v1, p.K) : nullptr;
         const uint16_t *asrc = arow ? reinterpret_cast<const uint16_t *>(arow) + kl

@@ -231,10 +231,10 @@ def test_fused_pool_bad_page_entry_reads_no_adapter():
 
 # ---------------------------------------------------------------------------
 # The fold at decode sizes: 64 x 64 tiles.  Each column tile carries 16 t
-# columns past its 64 W rows; column j of column tile tn is entry
-# tn + j * tiles (then cap + tn + j * tiles for the second pass) of the list
-# of every slot row (slice, adapter, rank < the slice's max_rank), so the
-# columns past an adapter's rank are computed too and must never be read.
+# columns past its 64 W rows; column j of column tile tn is entry 16 tn + j
+# (then cap + 16 tn + j for the second pass) of the list of every slot row
+# (slice, adapter, rank < the slice's max_rank), so the columns past an
+# adapter's rank are computed too and must never be read.
 # ---------------------------------------------------------------------------
 
 def check_fused_one(oracle_mod, w, pad, expect_shrink=0):
