@@ -1341,6 +1341,10 @@ hipError_t launch_gemm_fused(int64_t M, int64_t k, int64_t d, const void *x, int
   PipeArgs pa = pipe_args(M, k, d, x, ldx, W, ldw, y, ldy);
   pa.ft = ft;
   if (choose_tile(M, d) == 4) {
+    // the 64 x 64 tiles decode the list with an fp32 reciprocal of each
+    // slice's max_rank, exact up to 128 (the MFMA path takes at most 64)
+    for (int q = 0; q < ft.n_slices; ++q)
+      if (ft.R[q] < 0 || ft.R[q] > 128) return hipErrorInvalidValue;
     if (!launch_pipe<64, 64, 2, 2, kStages64, true>(pa, st, plan)) return hipErrorInvalidValue;
   } else if (split_ok(M, k, d, gws, gws_bytes)) {
     launch_split<true>(pa, M, d, gws, expired, st, plan);
