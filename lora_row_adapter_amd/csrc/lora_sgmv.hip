@@ -649,15 +649,19 @@ __device__ __forceinline__ void expand_body(const LoraArgs &a) {
 // 64-column units per wave.  One: the waves are co-resident and wait on
 // memory, so more of them in flight beats more loads per wave (4 units at
 // the 70B q+v shape: 14.3 -> 22.7 us); 80 VGPRs give six waves per SIMD.
-// A workgroup's four waves take four consecutive items over the same
+// A workgroup's ITEMS waves take as many consecutive items over the same
 // columns: items of one adapter are consecutive, so they read the same B_s
 // rows and all but the first find them in the CU's cache (B loads were the
-// largest part of this kernel's time: 14.3 -> 9.8 us without them).
+// largest part of this kernel's time: 14.3 -> 9.8 us without them).  Eight
+// items per workgroup where the slots' padded B lines are shared and the
+// grid still fills the CUs twice over (measured: 70B q+v 13.0 -> 12.3 us;
+// with fewer workgroups, decode-4096 5.5 -> 5.9 us, and with a pool's
+// single-item adapters, paged pool 26.0 -> 27.3 us), else four.
 constexpr int kW16Units = 1;
 constexpr int kW16Cols = 64 * kW16Units;        // columns per workgroup
-constexpr int kW16Items = 4;                    // items per workgroup (one per wave)
-template <int RMX, bool POOL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void k_expand_w16(LoraArgs a) {
+template <int RMX, bool POOL, int ITEMS>
+__global__ __launch_bounds__(64 * ITEMS) __attribute__((amdgpu_waves_per_eu(6))) void k_expand_w16(LoraArgs a) {
+  constexpr int kW16Items = ITEMS;  // items per workgroup (one per wave)
   constexpr int NU = kW16Units;
   const int ncb = a.col_blk[a.n_slices];  // kW16Cols-column blocks over all slices
   const int per_xcd = (ncb + 7) >> 3;
@@ -1173,13 +1177,18 @@ hipError_t launch_expand_sgmv(const LoraArgs &a0, int rows_per_item, hipStream_t
     for (int q = 0; q < a.n_slices; ++q)
       a.col_blk[q + 1] = a.col_blk[q] + (int32_t)((a.sl[q].d + kW16Cols - 1) / kW16Cols);
     const int64_t wb8 = ((int64_t)a.col_blk[a.n_slices] + 7) / 8 * 8;
-    const dim3 grid((unsigned)((a.L.items_g_cap + kW16Items - 1) / kW16Items * wb8));
+    auto grid_of = [&](int items) {
+      return dim3((unsigned)((a.L.items_g_cap + items - 1) / items * wb8));
+    };
     if (pooled) {
-      if (r32) hipLaunchKernelGGL((k_expand_w16<32, true>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_expand_w16<RMAX_MFMA, true>), grid, dim3(256), 0, st, a);
+      if (r32) hipLaunchKernelGGL((k_expand_w16<32, true, 4>), grid_of(4), dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_expand_w16<RMAX_MFMA, true, 4>), grid_of(4), dim3(256), 0, st, a);
+    } else if (grid_of(8).x >= 512) {
+      if (r32) hipLaunchKernelGGL((k_expand_w16<32, false, 8>), grid_of(8), dim3(512), 0, st, a);
+      else hipLaunchKernelGGL((k_expand_w16<RMAX_MFMA, false, 8>), grid_of(8), dim3(512), 0, st, a);
     } else {
-      if (r32) hipLaunchKernelGGL((k_expand_w16<32, false>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_expand_w16<RMAX_MFMA, false>), grid, dim3(256), 0, st, a);
+      if (r32) hipLaunchKernelGGL((k_expand_w16<32, false, 4>), grid_of(4), dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_expand_w16<RMAX_MFMA, false, 4>), grid_of(4), dim3(256), 0, st, a);
     }
   } else if (rows_per_item == 16)
     expand_pick<16>(a, mode, r32, dim3((unsigned)(a.L.items_g_cap * cb8)), st);
